@@ -1,0 +1,41 @@
+"""fp64 CPU oracle for the FlashBlock attention step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The
+product path (the ``cached_attention_amd`` package and its HIP library) never
+imports, links or runs this package, and this package never imports the product
+path: the two share no code.  Inputs come from ``cached_attention_amd.workloads``
+(seeded draws only, no attention arithmetic) or from the tests themselves.
+
+Source of what is computed: the FlashBlock pages -- the explainer page
+"FlashBlock: Attention Caching for Efficient Long-Context Block Diffusion"
+(Technical Summary section 2, "Core Mechanism", its merge equation, and
+"Adaptive Reuse Strategies") and the FlashBlock abstract.  Where the pages
+leave a step open, the reading taken is stated at the function that takes it.
+
+Pins (tests/test_oracle_pins.py): brute force on tiny inputs, the CPU fp64
+``scaled_dot_product_attention`` and ``logsumexp`` library routines (with their
+own GQA convention), hand-derived worked examples under ``tests/golden/``,
+closed forms (zero keys, constant values, a single key, score shifts, key
+permutations), the partition invariant of the merge, cached mode at r = 1
+against full recompute, and the refresh schedule.  Cached mode at r > 1 is an
+approximation the pages define only as a procedure: its values are pinned only
+through those building blocks ("parity unpinned" for the drift values).
+"""
+from .attention import (  # noqa: F401
+    NEG_INF,
+    partial_attention,
+    merge,
+    kv_group,
+    prefix_token_sets,
+    prefix_partial,
+    block_partial,
+    merge_outputs,
+    full_step,
+    run_block,
+    refresh_due,
+    to_output_layout,
+    sparse_only_step,
+    grow_prefix,
+    BlockResult,
+)
