@@ -1,0 +1,408 @@
+// Host side of libflashblock.so: argument validation, split planning and the
+// C ABI declared in include/flashblock.h.  Every check runs before anything is
+// enqueued; the library allocates nothing and keeps no state between calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "fb_internal.h"
+#include "flashblock.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fb_status fail(fb_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+// MI355X: 256 compute units.  Split planning targets whole waves of
+// workgroups over them; the constant keeps plans (and workspace sizes)
+// independent of the calling thread's device state.
+constexpr int kCUs = 256;
+constexpr int kMinSplitTiles = 4;  // >= 256 keys per split
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(const fb_desc* d) { return d->dtype == FB_BF16 ? 2 : 4; }
+
+// Query rows per workgroup for the prefix pass (bf16: 64 * qt).
+int prefix_qt(const fb_desc* d) {
+  const int rows = (d->hq / d->hkv) * d->block_len;
+  if (d->dtype == FB_F32) return 1;
+  return rows <= 64 ? 1 : rows <= 128 ? 2 : 4;
+}
+int block_qt(const fb_desc* d) {
+  const int rows = (d->hq / d->hkv) * d->block_len;
+  if (d->dtype == FB_F32) return 1;
+  return rows >= 512 ? 2 : 1;
+}
+// Workgroups resident per CU for a given row tile (register / LDS limits).
+int wgs_per_cu(const fb_desc* d, int qt) {
+  if (d->dtype == FB_F32) return 2;
+  return qt >= 2 ? 1 : 2;
+}
+
+fb_status check_desc(const fb_desc* d) {
+  if (!d) return fail(FB_ERR_NULL, "fb_desc is NULL");
+  if (d->abi_version != FB_ABI_VERSION)
+    return fail(FB_ERR_ARG, "abi_version %d != %d", d->abi_version, FB_ABI_VERSION);
+  if (d->dtype != FB_F32 && d->dtype != FB_BF16)
+    return fail(FB_ERR_UNSUPPORTED, "dtype %d not supported (FB_F32, FB_BF16)", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(FB_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)", d->head_dim);
+  if (d->batch < 1 || d->hq < 1 || d->hkv < 1 || d->block_len < 1)
+    return fail(FB_ERR_SHAPE, "batch, hq, hkv and block_len must be >= 1 (got %d, %d, %d, %d)", d->batch,
+                d->hq, d->hkv, d->block_len);
+  if (d->hq % d->hkv != 0) return fail(FB_ERR_SHAPE, "hq %d is not a multiple of hkv %d", d->hq, d->hkv);
+  const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
+  if (rows > (1LL << 30) || (int64_t)(d->hq / d->hkv) * d->block_len > (1 << 24))
+    return fail(FB_ERR_SHAPE, "batch * hq * block_len too large");
+  if (!isfinite(d->softmax_scale)) return fail(FB_ERR_ARG, "softmax_scale is not finite");
+  const int64_t e = esize(d);
+  const int64_t strides[] = {d->q_stride_b, d->q_stride_t, d->q_stride_h, d->kv_stride_b, d->kv_stride_t,
+                             d->kv_stride_h, d->pre_stride_t, d->pre_stride_h};
+  for (int64_t s : strides) {
+    if (s < 0) return fail(FB_ERR_SHAPE, "negative stride %lld", (long long)s);
+    if ((s * e) % 16 != 0)
+      return fail(FB_ERR_ALIGN, "stride %lld elements is not a multiple of 16 bytes", (long long)s);
+  }
+  return FB_OK;
+}
+
+int64_t total_prefix(const fb_desc* d) { return d->prefix_offsets_host[d->batch] - d->prefix_offsets_host[0]; }
+
+fb_status check_offsets(const fb_desc* d) {
+  if (!d->prefix_offsets_host || !d->prefix_offsets_dev)
+    return fail(FB_ERR_NULL, "prefix_offsets_host and prefix_offsets_dev are required");
+  const int64_t* o = d->prefix_offsets_host;
+  if (o[0] < 0) return fail(FB_ERR_SHAPE, "prefix offset[0] = %lld < 0", (long long)o[0]);
+  for (int b = 0; b < d->batch; ++b) {
+    if (o[b + 1] < o[b])
+      return fail(FB_ERR_SHAPE, "prefix offsets decrease at stream %d (%lld -> %lld)", b, (long long)o[b],
+                  (long long)o[b + 1]);
+    if (o[b + 1] - o[b] > (1LL << 30)) return fail(FB_ERR_SHAPE, "prefix of stream %d too long", b);
+  }
+  return FB_OK;
+}
+
+fb_status check_sparse(const fb_sparse* sp, bool need_mode) {
+  if (!sp) return FB_OK;
+  if (!sp->chunk_idx_dev) return fail(FB_ERR_NULL, "fb_sparse.chunk_idx_dev is NULL");
+  if (sp->k < 1) return fail(FB_ERR_ARG, "fb_sparse.k = %d < 1", sp->k);
+  if (sp->chunk_len < 64 || sp->chunk_len % 64 != 0)
+    return fail(FB_ERR_ARG, "fb_sparse.chunk_len = %d is not a positive multiple of 64", sp->chunk_len);
+  if (need_mode && sp->mode != FB_CHUNKS_SELECTED && sp->mode != FB_CHUNKS_COMPLEMENT)
+    return fail(FB_ERR_ARG, "fb_sparse.mode = %d (FB_CHUNKS_SELECTED or FB_CHUNKS_COMPLEMENT)", sp->mode);
+  if ((int64_t)sp->k * (sp->chunk_len / 64) > (1 << 28)) return fail(FB_ERR_ARG, "fb_sparse.k too large");
+  return FB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// split plan of the prefix pass
+// ---------------------------------------------------------------------------
+
+struct PrefixPlan {
+  int qt, row_tiles, split_tiles, total_splits, n_work, grid;
+  int chunk_mode, n_sel, chunk_tiles;
+  size_t part_o_bytes, part_lse_bytes;
+};
+
+int64_t logical_tiles_host(const fb_desc* d, int b, int chunk_mode, int n_sel, int chunk_tiles) {
+  if (chunk_mode == fb::CHUNKS_SELECTED) return (int64_t)n_sel * chunk_tiles;
+  const int64_t lp = d->prefix_offsets_host[b + 1] - d->prefix_offsets_host[b];
+  return ceil_div(lp, fb::kTile);
+}
+
+fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len, PrefixPlan* p) {
+  const int rows = (d->hq / d->hkv) * d->block_len;
+  p->qt = prefix_qt(d);
+  const int rows_per_wg = d->dtype == FB_F32 ? 64 : 64 * p->qt;
+  p->row_tiles = (int)ceil_div(rows, rows_per_wg);
+  p->chunk_mode = chunk_mode;
+  p->n_sel = n_sel;
+  p->chunk_tiles = chunk_mode == fb::CHUNKS_ALL ? 1 : chunk_len / fb::kTile;
+  const int64_t units = (int64_t)d->hkv * p->row_tiles;
+  int64_t total_tiles = 0;
+  for (int b = 0; b < d->batch; ++b) total_tiles += logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles);
+  const int64_t target = (int64_t)kCUs * wgs_per_cu(d, p->qt);
+  int64_t st = std::max<int64_t>(kMinSplitTiles, ceil_div(total_tiles * units, target));
+  if (st > (1 << 28)) st = 1 << 28;
+  p->split_tiles = (int)st;
+  int64_t splits = 0;
+  for (int b = 0; b < d->batch; ++b)
+    splits += ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles), st);
+  const int64_t work = splits * units;
+  if (work > (1LL << 30)) return fail(FB_ERR_SHAPE, "prefix pass needs too many workgroups");
+  p->total_splits = (int)splits;
+  p->n_work = (int)work;
+  p->grid = (int)ceil_div(work, 8) * 8;
+  const size_t prow = (size_t)splits * d->hq * d->block_len;
+  p->part_o_bytes = align_up(prow * d->head_dim * sizeof(float));
+  p->part_lse_bytes = align_up(prow * sizeof(float));
+  return FB_OK;
+}
+
+float c_log2(const fb_desc* d) {
+  const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return scale * 1.4426950408889634f;
+}
+
+void fill_common(const fb_desc* d, const void* q, fb::AttnArgs* a) {
+  memset(a, 0, sizeof(*a));
+  a->q = q;
+  a->q_sb = d->q_stride_b;
+  a->q_st = d->q_stride_t;
+  a->q_sh = d->q_stride_h;
+  a->B = d->batch;
+  a->Hq = d->hq;
+  a->Hkv = d->hkv;
+  a->G = d->hq / d->hkv;
+  a->Lb = d->block_len;
+  a->rows = a->G * d->block_len;
+  a->c_log2 = c_log2(d);
+}
+
+fb_status hip_status(int err, const char* what) {
+  if (err != 0) return fail(FB_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+  return FB_OK;
+}
+
+// Prefix pass with a chosen chunk mode; `extra_*` (nullable) is one more
+// partial folded into the combine (the sparse residual).
+fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
+                     const fb_sparse* sp, const float* extra_o, const float* extra_lse, float* o_ext,
+                     float* lse_ext, void* ws, size_t ws_bytes, void* stream) {
+  PrefixPlan p;
+  const int n_sel = sp ? sp->k : 0;
+  const int chunk_len = sp ? sp->chunk_len : 64;
+  fb_status st = plan_prefix(d, chunk_mode, n_sel, chunk_len, &p);
+  if (st != FB_OK) return st;
+  if (p.part_o_bytes + p.part_lse_bytes > ws_bytes)
+    return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.part_o_bytes + p.part_lse_bytes);
+  float* part_o = (float*)ws;
+  float* part_lse = (float*)((char*)ws + p.part_o_bytes);
+  fb::AttnArgs a;
+  fill_common(d, q, &a);
+  a.k = k_pre;
+  a.v = v_pre;
+  a.kv_st = d->pre_stride_t;
+  a.kv_sh = d->pre_stride_h;
+  a.offsets = d->prefix_offsets_dev;
+  a.split_tiles = p.split_tiles;
+  a.row_tiles = p.row_tiles;
+  a.n_work = p.n_work;
+  a.grid = p.grid;
+  a.chunks = sp ? sp->chunk_idx_dev : nullptr;
+  a.n_sel = n_sel;
+  a.chunk_tiles = p.chunk_tiles;
+  a.chunk_mode = chunk_mode;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  st = hip_status(fb::launch_attn(a, d->dtype, d->head_dim, p.qt, true, stream), "prefix attention launch");
+  if (st != FB_OK) return st;
+  fb::CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.part_o = part_o;
+  c.part_lse = part_lse;
+  c.offsets = d->prefix_offsets_dev;
+  c.B = d->batch;
+  c.Hq = d->hq;
+  c.Lb = d->block_len;
+  c.D = d->head_dim;
+  c.split_tiles = p.split_tiles;
+  c.n_sel = n_sel;
+  c.chunk_tiles = p.chunk_tiles;
+  c.chunk_mode = chunk_mode;
+  c.total_splits = p.total_splits;
+  c.extra_o = extra_o;
+  c.extra_lse = extra_lse;
+  c.o = o_ext;
+  c.lse = lse_ext;
+  const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
+  return hip_status(fb::launch_combine(c, rows, stream), "split combine launch");
+}
+
+fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const void* v_blk, const float* o_ext,
+                    const float* lse_ext, void* o, float* lse_out, void* stream) {
+  fb::AttnArgs a;
+  fill_common(d, q, &a);
+  a.k = k_blk;
+  a.v = v_blk;
+  a.kv_sb = d->kv_stride_b;
+  a.kv_st = d->kv_stride_t;
+  a.kv_sh = d->kv_stride_h;
+  a.offsets = nullptr;
+  const int qt = block_qt(d);
+  const int rows_per_wg = d->dtype == FB_F32 ? 64 : 64 * qt;
+  a.row_tiles = (int)ceil_div(a.rows, rows_per_wg);
+  a.split_tiles = (int)ceil_div(d->block_len, fb::kTile);
+  const int64_t work = (int64_t)d->batch * d->hkv * a.row_tiles;
+  if (work > (1LL << 30)) return fail(FB_ERR_SHAPE, "block pass needs too many workgroups");
+  a.n_work = (int)work;
+  a.grid = (int)ceil_div(work, 8) * 8;
+  a.ext_o = o_ext;
+  a.ext_lse = lse_ext;
+  a.o = o;
+  a.lse_out = lse_out;
+  return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, qt, false, stream), "block attention launch");
+}
+
+size_t workspace_for(const fb_desc* d, const fb_sparse* sp) {
+  PrefixPlan p;
+  size_t need = 0;
+  if (!sp) {
+    if (plan_prefix(d, fb::CHUNKS_ALL, 0, 64, &p) != FB_OK) return 0;
+    need = p.part_o_bytes + p.part_lse_bytes;
+  } else {
+    for (int mode : {fb::CHUNKS_SELECTED, fb::CHUNKS_COMPLEMENT}) {
+      if (plan_prefix(d, mode, sp->k, sp->chunk_len, &p) != FB_OK) return 0;
+      need = std::max(need, p.part_o_bytes + p.part_lse_bytes);
+    }
+  }
+  return std::max<size_t>(need, kAlign);
+}
+
+fb_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!ws) return fail(FB_ERR_NULL, "workspace is NULL");
+  if (((uintptr_t)ws % kAlign) != 0) return fail(FB_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return FB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fb_abi_version(void) { return FB_ABI_VERSION; }
+
+const char* fb_last_error(void) { return g_err; }
+
+const char* fb_status_string(fb_status s) {
+  switch (s) {
+    case FB_OK: return "ok";
+    case FB_ERR_NULL: return "null pointer";
+    case FB_ERR_SHAPE: return "bad shape";
+    case FB_ERR_ALIGN: return "misaligned pointer or stride";
+    case FB_ERR_WORKSPACE: return "workspace too small";
+    case FB_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+    case FB_ERR_ARG: return "bad argument";
+    case FB_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp) {
+  clear_error();
+  if (check_desc(d) != FB_OK || check_offsets(d) != FB_OK || check_sparse(sp, false) != FB_OK) return 0;
+  return workspace_for(d, sp);
+}
+
+fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
+                         const fb_sparse* sp, float* o_ext, float* lse_ext, void* ws, size_t ws_bytes,
+                         void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st != FB_OK) return st;
+  if (!q_blk || !o_ext || !lse_ext) return fail(FB_ERR_NULL, "q_blk, o_ext and lse_ext are required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre) || !aligned16(o_ext))
+    return fail(FB_ERR_ALIGN, "q_blk, k_pre, v_pre and o_ext must be 16-byte aligned");
+  const size_t need = workspace_for(d, sp);
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+  const int mode = sp ? sp->mode : fb::CHUNKS_ALL;
+  return run_prefix(d, q_blk, k_pre, v_pre, mode, sp, nullptr, nullptr, o_ext, lse_ext, ws, ws_bytes, stream);
+}
+
+fb_status fb_block_attn(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                        const float* o_ext, const float* lse_ext, void* o, float* lse_out, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st != FB_OK) return st;
+  if (!q_blk || !k_blk || !v_blk || !o) return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk and o are required");
+  if ((o_ext == nullptr) != (lse_ext == nullptr))
+    return fail(FB_ERR_NULL, "o_ext and lse_ext must be both given or both NULL");
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+      (o_ext && !aligned16(o_ext)))
+    return fail(FB_ERR_ALIGN, "q_blk, k_blk, v_blk, o and o_ext must be 16-byte aligned");
+  return run_block(d, q_blk, k_blk, v_blk, o_ext, lse_ext, o, lse_out, stream);
+}
+
+fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a, const float* o_b,
+                   const float* lse_b, float* o, float* lse, void* stream) {
+  clear_error();
+  if (rows < 0 || rows > (1LL << 36)) return fail(FB_ERR_SHAPE, "rows = %lld out of range", (long long)rows);
+  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
+    return fail(FB_ERR_UNSUPPORTED, "head_dim %d must be a multiple of 4 in [4, 1024]", head_dim);
+  if (rows == 0) return FB_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return fail(FB_ERR_NULL, "fb_merge: NULL pointer");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return fail(FB_ERR_ALIGN, "fb_merge: o_a, o_b, o must be 16-byte aligned");
+  return hip_status(fb::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, o, lse, stream), "merge launch");
+}
+
+fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
+                  const void* v_pre, const fb_sparse* sp, float* o_ext_cache, float* lse_ext_cache,
+                  float* o_res_cache, float* lse_res_cache, void* o, float* lse_out, int32_t step,
+                  int32_t refresh_period, int32_t mode, int32_t force_refresh, int32_t* refreshed_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, false);
+  if (st != FB_OK) return st;
+  if (step < 0) return fail(FB_ERR_ARG, "step = %d < 0", step);
+  if (refresh_period < 1) return fail(FB_ERR_ARG, "refresh_period = %d < 1", refresh_period);
+  if (mode != FB_MODE_CACHED && mode != FB_MODE_FULL) return fail(FB_ERR_ARG, "mode = %d", mode);
+  if (!q_blk || !k_blk || !v_blk || !o_ext_cache || !lse_ext_cache || !o)
+    return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache and o are required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (sp && (!o_res_cache || !lse_res_cache))
+    return fail(FB_ERR_NULL, "the sparse variant needs o_res_cache and lse_res_cache");
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pre) || !aligned16(v_pre) ||
+      !aligned16(o_ext_cache) || !aligned16(o) || (sp && !aligned16(o_res_cache)))
+    return fail(FB_ERR_ALIGN, "all tensor base pointers must be 16-byte aligned");
+  const size_t need = workspace_for(d, sp);
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+
+  const bool refresh = mode == FB_MODE_FULL || force_refresh != 0 || step % refresh_period == 0;
+  if (refreshed_out) *refreshed_out = refresh ? 1 : 0;
+  if (!sp) {
+    if (refresh) {
+      st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_ALL, nullptr, nullptr, nullptr, o_ext_cache,
+                      lse_ext_cache, ws, ws_bytes, stream);
+      if (st != FB_OK) return st;
+    }
+  } else {
+    if (refresh) {
+      st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_COMPLEMENT, sp, nullptr, nullptr, o_res_cache,
+                      lse_res_cache, ws, ws_bytes, stream);
+      if (st != FB_OK) return st;
+    }
+    st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_SELECTED, sp, o_res_cache, lse_res_cache, o_ext_cache,
+                    lse_ext_cache, ws, ws_bytes, stream);
+    if (st != FB_OK) return st;
+  }
+  return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
+}
+
+}  // extern "C"

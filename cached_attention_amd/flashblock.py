@@ -1,0 +1,208 @@
+"""ctypes binding of libflashblock.so (include/flashblock.h), argument marshalling only.
+
+Every entry point keeps the C name and argument order.  Tensor arguments may be
+torch tensors (their data pointer is passed) or plain integer addresses; the
+stream defaults to torch's current stream on the current device.  A non-zero
+status raises ``FlashBlockError`` carrying fb_last_error().  Nothing here
+computes attention: every step runs in the HIP library, and importing a
+function from here fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashblock.so")
+
+FB_ABI_VERSION = 1
+FB_OK, FB_ERR_NULL, FB_ERR_SHAPE, FB_ERR_ALIGN, FB_ERR_WORKSPACE, FB_ERR_UNSUPPORTED, FB_ERR_ARG, FB_ERR_HIP = range(8)
+FB_F32, FB_BF16 = 0, 1
+FB_MODE_CACHED, FB_MODE_FULL = 0, 1
+FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
+
+EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_merge", "fb_step",
+           "fb_status_string", "fb_last_error", "fb_abi_version")
+
+
+class FlashBlockError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class fb_desc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("hq", ctypes.c_int32),
+        ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_len", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("prefix_offsets_host", ctypes.POINTER(ctypes.c_int64)),
+        ("prefix_offsets_dev", ctypes.c_void_p),
+        ("q_stride_b", ctypes.c_int64), ("q_stride_t", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("kv_stride_b", ctypes.c_int64), ("kv_stride_t", ctypes.c_int64), ("kv_stride_h", ctypes.c_int64),
+        ("pre_stride_t", ctypes.c_int64), ("pre_stride_h", ctypes.c_int64),
+    ]
+
+
+class fb_sparse(ctypes.Structure):
+    _fields_ = [
+        ("chunk_idx_dev", ctypes.c_void_p),
+        ("k", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m cached_attention_amd.build`")
+        l = ctypes.CDLL(_LIB_PATH)
+        P, D, S = ctypes.c_void_p, ctypes.POINTER(fb_desc), ctypes.POINTER(fb_sparse)
+        i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        l.fb_workspace_size.argtypes = [D, S]
+        l.fb_workspace_size.restype = sz
+        l.fb_prefix_attn.argtypes = [D, P, P, P, S, P, P, P, sz, P]
+        l.fb_prefix_attn.restype = i32
+        l.fb_block_attn.argtypes = [D, P, P, P, P, P, P, P, P]
+        l.fb_block_attn.restype = i32
+        l.fb_merge.argtypes = [i64, i32, P, P, P, P, P, P, P]
+        l.fb_merge.restype = i32
+        l.fb_step.argtypes = [D, P, P, P, P, P, S, P, P, P, P, P, P, i32, i32, i32, i32,
+                              ctypes.POINTER(i32), P, sz, P]
+        l.fb_step.restype = i32
+        l.fb_status_string.argtypes = [i32]
+        l.fb_status_string.restype = ctypes.c_char_p
+        l.fb_last_error.argtypes = []
+        l.fb_last_error.restype = ctypes.c_char_p
+        l.fb_abi_version.argtypes = []
+        l.fb_abi_version.restype = i32
+        if l.fb_abi_version() != FB_ABI_VERSION:
+            raise ImportError(f"libflashblock ABI {l.fb_abi_version()} != binding ABI {FB_ABI_VERSION}")
+        _lib = l
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != FB_OK:
+        raise FlashBlockError(status, where, lib().fb_last_error().decode())
+
+
+class Desc:
+    """Owns an fb_desc plus the host offsets array it points to."""
+
+    def __init__(self, dtype: int, batch: int, hq: int, hkv: int, head_dim: int, block_len: int,
+                 prefix_offsets_host: Sequence[int], prefix_offsets_dev=None, softmax_scale: float = 0.0,
+                 q_strides: Optional[Sequence[int]] = None, kv_strides: Optional[Sequence[int]] = None,
+                 pre_strides: Optional[Sequence[int]] = None):
+        self._off = np.ascontiguousarray(np.asarray(prefix_offsets_host, dtype=np.int64))
+        self._off_dev = prefix_offsets_dev      # keeps a tensor alive
+        d = fb_desc()
+        d.abi_version = FB_ABI_VERSION
+        d.dtype, d.batch, d.hq, d.hkv = dtype, batch, hq, hkv
+        d.head_dim, d.block_len, d.softmax_scale = head_dim, block_len, softmax_scale
+        d.prefix_offsets_host = self._off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        d.prefix_offsets_dev = _ptr(prefix_offsets_dev)
+        qs = q_strides or (block_len * hq * head_dim, hq * head_dim, head_dim)
+        ks = kv_strides or (block_len * hkv * head_dim, hkv * head_dim, head_dim)
+        ps = pre_strides or (hkv * head_dim, head_dim)
+        d.q_stride_b, d.q_stride_t, d.q_stride_h = qs
+        d.kv_stride_b, d.kv_stride_t, d.kv_stride_h = ks
+        d.pre_stride_t, d.pre_stride_h = ps
+        self.c = d
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class Sparse:
+    def __init__(self, chunk_idx_dev, k: int, chunk_len: int = 64, mode: int = FB_CHUNKS_SELECTED):
+        self._idx = chunk_idx_dev
+        s = fb_sparse()
+        s.chunk_idx_dev = _ptr(chunk_idx_dev)
+        s.k, s.chunk_len, s.mode = k, chunk_len, mode
+        self.c = s
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _sref(sparse):
+    return None if sparse is None else sparse.ref
+
+
+def fb_workspace_size(desc: Desc, sparse: Optional[Sparse] = None) -> int:
+    n = lib().fb_workspace_size(desc.ref, _sref(sparse))
+    if n == 0:
+        raise FlashBlockError(FB_ERR_ARG, "fb_workspace_size", lib().fb_last_error().decode())
+    return n
+
+
+def fb_prefix_attn(desc: Desc, q_blk, k_pre, v_pre, sparse: Optional[Sparse], o_ext, lse_ext, ws,
+                   ws_bytes: int, stream=None) -> None:
+    _check(lib().fb_prefix_attn(desc.ref, _ptr(q_blk), _ptr(k_pre), _ptr(v_pre), _sref(sparse), _ptr(o_ext),
+                                _ptr(lse_ext), _ptr(ws), ws_bytes, _stream(stream)), "fb_prefix_attn")
+
+
+def fb_block_attn(desc: Desc, q_blk, k_blk, v_blk, o_ext, lse_ext, o, lse_out=None, stream=None) -> None:
+    _check(lib().fb_block_attn(desc.ref, _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(o_ext), _ptr(lse_ext),
+                               _ptr(o), _ptr(lse_out), _stream(stream)), "fb_block_attn")
+
+
+def fb_merge(rows: int, head_dim: int, o_a, lse_a, o_b, lse_b, o, lse, stream=None) -> None:
+    _check(lib().fb_merge(rows, head_dim, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
+                          _stream(stream)), "fb_merge")
+
+
+def fb_step(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, sparse: Optional[Sparse], o_ext_cache,
+            lse_ext_cache, o_res_cache, lse_res_cache, o, lse_out, step: int, refresh_period: int,
+            mode: int, force_refresh: bool, ws, ws_bytes: int, stream=None) -> bool:
+    """Returns True if this step refreshed the block-external cache."""
+    refreshed = ctypes.c_int32(0)
+    _check(lib().fb_step(desc.ref, _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre),
+                         _sref(sparse), _ptr(o_ext_cache), _ptr(lse_ext_cache), _ptr(o_res_cache),
+                         _ptr(lse_res_cache), _ptr(o), _ptr(lse_out), step, refresh_period, mode,
+                         int(bool(force_refresh)), ctypes.byref(refreshed), _ptr(ws), ws_bytes,
+                         _stream(stream)), "fb_step")
+    return bool(refreshed.value)
+
+
+def fb_status_string(status: int) -> str:
+    return lib().fb_status_string(status).decode()
+
+
+def fb_last_error() -> str:
+    return lib().fb_last_error().decode()
+
+
+def fb_abi_version() -> int:
+    return lib().fb_abi_version()

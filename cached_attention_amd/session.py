@@ -1,0 +1,62 @@
+"""Device buffers for one attention layer shape, driven through fb_step.
+
+``AttentionStep`` allocates (with torch) the block-external cache, the sparse
+residual cache, the split workspace and the output for one shape, and runs
+denoising steps through the C ABI.  It adds no arithmetic of its own.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import flashblock as fbl
+
+_DT = {"bf16": (fbl.FB_BF16, torch.bfloat16), "f32": (fbl.FB_F32, torch.float32)}
+
+
+class AttentionStep:
+    def __init__(self, dtype: str, batch: int, hq: int, hkv: int, head_dim: int, block_len: int,
+                 prefix_offsets: Sequence[int], device="cuda", chunks: Optional[torch.Tensor] = None,
+                 chunk_len: int = 64, softmax_scale: float = 0.0, pre_strides=None):
+        code, tdt = _DT[dtype]
+        self.dtype, self.tdtype = dtype, tdt
+        self.shape = (batch, hq, hkv, head_dim, block_len)
+        self.offsets = np.asarray(prefix_offsets, dtype=np.int64)
+        self.off_dev = torch.tensor(self.offsets, dtype=torch.int64, device=device)
+        self.desc = fbl.Desc(code, batch, hq, hkv, head_dim, block_len, self.offsets, self.off_dev,
+                             softmax_scale=softmax_scale, pre_strides=pre_strides)
+        self.sparse = None
+        if chunks is not None:
+            self.chunks = chunks.to(device=device, dtype=torch.int32).contiguous()
+            self.sparse = fbl.Sparse(self.chunks, int(self.chunks.shape[-1]), chunk_len)
+        self.ws_bytes = fbl.fb_workspace_size(self.desc, self.sparse)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.o_ext = torch.zeros(batch, hq, block_len, head_dim, **f32)
+        self.lse_ext = torch.full((batch, hq, block_len), float("-inf"), **f32)
+        self.o_res = self.lse_res = None
+        if self.sparse is not None:
+            self.o_res = torch.zeros(batch, hq, block_len, head_dim, **f32)
+            self.lse_res = torch.full((batch, hq, block_len), float("-inf"), **f32)
+        self.o = torch.empty(batch, block_len, hq, head_dim, dtype=tdt, device=device)
+        self.lse = torch.empty(batch, hq, block_len, **f32)
+
+    def step(self, q, k, v, k_pre, v_pre, step: int, refresh_period: int = 1, mode: str = "cached",
+             force_refresh: bool = False, want_lse: bool = True, stream=None) -> bool:
+        m = fbl.FB_MODE_FULL if mode == "full" else fbl.FB_MODE_CACHED
+        return fbl.fb_step(self.desc, q, k, v, k_pre, v_pre, self.sparse, self.o_ext, self.lse_ext,
+                           self.o_res, self.lse_res, self.o, self.lse if want_lse else None, step,
+                           refresh_period, m, force_refresh, self.ws, self.ws_bytes, stream)
+
+    def prefix(self, q, k_pre, v_pre, chunk_mode: Optional[int] = None, stream=None) -> None:
+        sp = None
+        if chunk_mode is not None:
+            sp = fbl.Sparse(self.chunks, int(self.chunks.shape[-1]), self.sparse.c.chunk_len, chunk_mode)
+        fbl.fb_prefix_attn(self.desc, q, k_pre, v_pre, sp, self.o_ext, self.lse_ext, self.ws, self.ws_bytes,
+                           stream)
+
+    def block(self, q, k, v, merge: bool = True, stream=None) -> None:
+        fbl.fb_block_attn(self.desc, q, k, v, self.o_ext if merge else None, self.lse_ext if merge else None,
+                          self.o, self.lse, stream)

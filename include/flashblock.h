@@ -1,0 +1,168 @@
+/*
+ * flashblock.h -- C ABI of libflashblock.so: the FlashBlock attention step for
+ * block diffusion on MI355X (gfx950).
+ *
+ * What is computed.  In block diffusion the queries of the active block attend
+ * to the KV cache of all earlier, finalised blocks (the prefix, J_out) and to
+ * the block's own keys and values (J_in).  FlashBlock (explainer page
+ * "FlashBlock: Attention Caching for Efficient Long-Context Block Diffusion",
+ * Technical Summary section 2, "Core Mechanism") splits the attention output
+ * into a block-external partial A_out with log-normaliser L_out = log Z_out and
+ * a block-internal partial A_in with L_in, keeps (A_out, L_out) from an earlier
+ * denoising step, recomputes only A_in, and recombines them exactly with the
+ * page's merge equation
+ *     m = max(L_out, L_in),
+ *     A = (e^(L_out-m) A_out + e^(L_in-m) A_in) / (e^(L_out-m) + e^(L_in-m)).
+ * The sparse variant (same page, "Adaptive Reuse Strategies", compatibility
+ * with sparse attention) caches the contribution of the keys a sparse selector
+ * leaves out as a residual partial and merges it with a fresh partial over the
+ * selected keys.
+ *
+ * Conventions (readings of points the pages leave open):
+ *   - softmax scale 1/sqrt(D) unless fb_desc.softmax_scale > 0;
+ *   - every L / LSE crossing this ABI is a natural log; an empty key set has
+ *     A = 0 and L = -inf;
+ *   - attention inside the block is bidirectional (no mask);
+ *   - query head h reads KV head h / (hq / hkv).
+ *
+ * Layouts (element strides; the head_dim axis is always contiguous):
+ *   q_blk  [B][Lb][Hq][D]   strides q_stride_{b,t,h}        dtype
+ *   k_blk, v_blk [B][Lb][Hkv][D]  strides kv_stride_{b,t,h}  dtype
+ *   k_pre, v_pre  packed ragged prefix: row t of KV head g of stream b sits at
+ *                 base + (off[b] + t) * pre_stride_t + g * pre_stride_h
+ *                 (token-major [T][Hkv][D] and head-major [Hkv][T][D] both fit)
+ *   o      [B][Lb][Hq][D]   contiguous                      dtype
+ *   o_ext / o_res caches [B][Hq][Lb][D] contiguous fp32;
+ *   lse_ext / lse_res / lse_out [B][Hq][Lb] contiguous fp32.
+ *
+ * Ownership.  The caller allocates and owns every buffer (inputs, outputs,
+ * caches, workspace, device offsets).  The library never allocates, frees or
+ * synchronises device memory and keeps no state between calls.  All device
+ * work is enqueued asynchronously on the caller's stream (`stream` is a
+ * hipStream_t passed as void*; NULL is the null stream).
+ *
+ * Errors.  Arguments are validated before anything is enqueued: on an error
+ * nothing is launched, outputs are untouched, the status code says which check
+ * failed and fb_last_error() (thread-local) gives the detail.  A launch failure
+ * returns FB_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef FLASHBLOCK_H
+#define FLASHBLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FB_ABI_VERSION 1
+
+typedef int32_t fb_status;
+enum {
+  FB_OK = 0,
+  FB_ERR_NULL = 1,        /* a required pointer is NULL */
+  FB_ERR_SHAPE = 2,       /* inconsistent sizes: hq % hkv, batch, block_len, offsets, strides */
+  FB_ERR_ALIGN = 3,       /* a base pointer or stride breaks 16-byte row alignment */
+  FB_ERR_WORKSPACE = 4,   /* workspace smaller than fb_workspace_size() */
+  FB_ERR_UNSUPPORTED = 5, /* dtype or head_dim not built */
+  FB_ERR_ARG = 6,         /* bad step, refresh period, mode or chunk list */
+  FB_ERR_HIP = 7          /* the HIP runtime refused a launch */
+};
+
+enum { FB_F32 = 0, FB_BF16 = 1 };
+enum { FB_MODE_CACHED = 0, FB_MODE_FULL = 1 };
+enum { FB_CHUNKS_SELECTED = 1, FB_CHUNKS_COMPLEMENT = 2 };
+
+/* Shapes, strides and prefix offsets shared by every call. */
+typedef struct fb_desc {
+  int32_t abi_version;      /* must equal FB_ABI_VERSION */
+  int32_t dtype;            /* FB_F32 or FB_BF16: q/k/v (block and prefix) and o */
+  int32_t batch;            /* B >= 1 independent streams */
+  int32_t hq;               /* query heads */
+  int32_t hkv;              /* KV heads; hq % hkv == 0 */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t block_len;        /* Lb >= 1 tokens in the active block */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(D) */
+  const int64_t* prefix_offsets_host; /* [B+1] host copy: stream b owns prefix rows
+                                         off[b] .. off[b+1]-1; off[0] >= 0, non-decreasing */
+  const int64_t* prefix_offsets_dev;  /* [B+1] device copy of the same values */
+  int64_t q_stride_b, q_stride_t, q_stride_h;    /* q_blk */
+  int64_t kv_stride_b, kv_stride_t, kv_stride_h; /* k_blk, v_blk */
+  int64_t pre_stride_t, pre_stride_h;            /* k_pre, v_pre */
+} fb_desc;
+
+/* Chunk list of the sparse variant: the prefix is cut into chunks of chunk_len
+ * tokens (the last one of a stream may be shorter); for each (stream, KV head)
+ * `k` chunk indices are listed, ascending and unique, each < ceil(Lp_b/chunk_len).
+ * SELECTED attends to the listed chunks only, COMPLEMENT to every other prefix
+ * token (the unselected keys whose contribution is cached as the residual). */
+typedef struct fb_sparse {
+  const int32_t* chunk_idx_dev; /* [B][Hkv][k] int32, device */
+  int32_t k;                    /* chunks listed per (stream, KV head), >= 1 */
+  int32_t chunk_len;            /* a positive multiple of 64 */
+  int32_t mode;                 /* FB_CHUNKS_SELECTED or FB_CHUNKS_COMPLEMENT */
+} fb_sparse;
+
+/* Bytes of workspace fb_prefix_attn / fb_step need for this shape (split-KV
+ * partials).  `sp` may be NULL (dense prefix).  For fb_step in sparse mode pass
+ * the fb_sparse it will get; the larger of the SELECTED and COMPLEMENT plans is
+ * returned.  Returns 0 on invalid arguments (see fb_last_error()). */
+size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp);
+
+/* Block-external partial (Core Mechanism: A_out and L_out = log Z_out) of every
+ * block query over the prefix of its stream (or over the chunks `sp` picks),
+ * split over the prefix and recombined by log-sum-exp weighting.
+ * Writes o_ext [B][Hq][Lb][D] fp32 and lse_ext [B][Hq][Lb] fp32 (natural log;
+ * -inf and a zero row for an empty prefix).  `ws` is scratch for the split
+ * partials, at least fb_workspace_size(d, sp) bytes, 256-byte aligned. */
+fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre,
+                         const void* v_pre, const fb_sparse* sp, float* o_ext,
+                         float* lse_ext, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-internal attention (Core Mechanism: A_in over J_in, bidirectional)
+ * of every block query over the block's own keys, merged with (o_ext, lse_ext)
+ * by the merge equation when those are non-NULL (both or neither), written to
+ * o [B][Lb][Hq][D] in the input dtype; lse_out (nullable) receives the merged
+ * natural-log LSE [B][Hq][Lb]. */
+fb_status fb_block_attn(const fb_desc* d, const void* q_blk, const void* k_blk,
+                        const void* v_blk, const float* o_ext, const float* lse_ext,
+                        void* o, float* lse_out, void* stream);
+
+/* The merge equation on its own, row by row: rows x head_dim fp32 partials
+ * (o_a, lse_a) and (o_b, lse_b) -> (o, lse).  o / lse may alias either input.
+ * A row with both LSE = -inf yields o = 0, lse = -inf. */
+fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
+                   const float* o_b, const float* lse_b, float* o, float* lse, void* stream);
+
+/* One denoising step of the active block.
+ * Refresh iff mode == FB_MODE_FULL, or force_refresh != 0, or step % r == 0
+ * (step counts from 0 within the block, so step 0 always refreshes):
+ *   dense (sp == NULL): refresh -> fb_prefix_attn into (o_ext_cache, lse_ext_cache);
+ *                       every step -> fb_block_attn merged with the cache into o.
+ *   sparse (sp != NULL, sp->mode ignored): refresh -> the COMPLEMENT partial into
+ *                       (o_res_cache, lse_res_cache); every step -> the SELECTED
+ *                       partial merged with the residual into (o_ext_cache,
+ *                       lse_ext_cache), then the block partial merged into o.
+ * A step that does not refresh reads caches written by an earlier refresh step of
+ * the same block (same buffers); otherwise its result is undefined.
+ * refreshed_out (host, nullable) receives 1 if this step refreshed.  Full mode
+ * recomputes the prefix every step, i.e. the standard per-step attention over the
+ * whole KV cache plus the block. */
+fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                  const void* k_pre, const void* v_pre, const fb_sparse* sp,
+                  float* o_ext_cache, float* lse_ext_cache, float* o_res_cache,
+                  float* lse_res_cache, void* o, float* lse_out, int32_t step,
+                  int32_t refresh_period, int32_t mode, int32_t force_refresh,
+                  int32_t* refreshed_out, void* ws, size_t ws_bytes, void* stream);
+
+const char* fb_status_string(fb_status s);
+const char* fb_last_error(void);
+int32_t fb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHBLOCK_H */

@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # names the case before any GPU work starts, so a run that dies mid-test says which one
+    if "gpu" in request.keywords:
+        print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield

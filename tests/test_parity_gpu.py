@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: bf16 workloads max-abs 2e-2 on O, O_ext and LSE (bf16 inputs,
+fp32 accumulation); fp32 max-abs 1e-5 * max(1, max|O_oracle|).  Drift parity:
+|drift_gpu - drift_oracle| <= 2 * tol.  Every input comes from the seeded
+generator; every expected value from the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention import to_output_layout
+from cached_attention_amd import flashblock as fbl
+from cached_attention_amd import workloads as wl
+from cached_attention_amd.session import AttentionStep
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device="cuda", dtype=dtype)
+
+
+def tol(w, ref):
+    if w.dtype == "bf16":
+        return 2e-2
+    return 1e-5 * max(1.0, float(np.abs(ref).max()))
+
+
+def scale_of(w):
+    return 1.0 / math.sqrt(w.head_dim)
+
+
+class GpuRun:
+    def __init__(self):
+        self.out, self.lse, self.o_ext, self.lse_ext, self.refreshed = [], [], [], [], []
+
+
+def run_gpu(w, prefix, blk, r=1, mode="cached", chunks=None, st=None, k_pre=None, v_pre=None):
+    t = TDT[w.dtype]
+    if st is None:
+        st = AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets,
+                           chunks=None if chunks is None else torch.from_numpy(chunks))
+    kp = dev(prefix.k, t) if k_pre is None else k_pre
+    vp = dev(prefix.v, t) if v_pre is None else v_pre
+    res = GpuRun()
+    for s in range(blk.q.shape[0]):
+        q, k, v = dev(blk.q[s], t), dev(blk.k[s], t), dev(blk.v[s], t)
+        res.refreshed.append(st.step(q, k, v, kp, vp, s, r, mode))
+        torch.cuda.synchronize()
+        res.out.append(st.o.float().cpu().numpy().astype(np.float64))
+        res.lse.append(st.lse.cpu().numpy().astype(np.float64))
+        res.o_ext.append(st.o_ext.cpu().numpy().astype(np.float64))
+        res.lse_ext.append(st.lse_ext.cpu().numpy().astype(np.float64))
+    return res
+
+
+def check_block(w, prefix, blk, r, mode, chunks=None, check_cache=True):
+    scale = scale_of(w)
+    ref = oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r,
+                           mode=mode, chunks=chunks)
+    got = run_gpu(w, prefix, blk, r, mode, chunks)
+    for s in range(w.steps):
+        tl = tol(w, ref.out[s])
+        err = np.abs(got.out[s] - ref.out[s]).max()
+        assert err <= tl, f"step {s}: max|O - O_ref| = {err:.3e} > {tl:.1e}"
+        lerr = np.abs(got.lse[s] - ref.lse[s]).max()
+        assert lerr <= max(tl, 1e-5), f"step {s}: LSE err {lerr:.3e}"
+        assert got.refreshed[s] == ref.refreshed[s]
+        if check_cache and mode == "cached":
+            e1 = np.abs(got.o_ext[s] - ref.o_ext[s]).max()
+            finite = np.isfinite(ref.lse_ext[s])
+            assert np.array_equal(np.isfinite(got.lse_ext[s]), finite)
+            e2 = np.abs(got.lse_ext[s][finite] - ref.lse_ext[s][finite]).max() if finite.any() else 0.0
+            assert e1 <= tl and e2 <= max(tl, 1e-5), f"step {s}: cache err {e1:.3e} {e2:.3e}"
+    return ref, got
+
+
+# ---------------------------------------------------------------------------
+# every workload at CI sizes, exact and cached modes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r,mode", [(1, "cached"), (2, "cached"), (4, "cached"), (1, "full")])
+def test_tiny_f32(r, mode):
+    w = wl.WORKLOADS["tiny_f32"]
+    prefix, blocks = wl.make_inputs(w)
+    check_block(w, prefix, blocks[0], r, mode)
+
+
+@pytest.mark.parametrize("lp", [1000, 4096])
+@pytest.mark.parametrize("r,mode", [(1, "cached"), (4, "cached"), (8, "cached"), (1, "full")])
+def test_text_mha(lp, r, mode):
+    w = wl.ci_version(wl.WORKLOADS["text_mha_4k"], prefix_len=lp)
+    prefix, blocks = wl.make_inputs(w)
+    check_block(w, prefix, blocks[0], r, mode)
+
+
+@pytest.mark.parametrize("r,mode", [(1, "cached"), (8, "cached"), (1, "full")])
+def test_text_gqa(r, mode):
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=4100)
+    prefix, blocks = wl.make_inputs(w)
+    check_block(w, prefix, blocks[0], r, mode)
+
+
+@pytest.mark.parametrize("r", [1, 8])
+def test_text_gqa_sparse(r):
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=4100)   # 65 chunks, last one 4 tokens
+    prefix, blocks = wl.make_inputs(w)
+    chunks = wl.make_chunk_selection(w, prefix.lengths)
+    assert chunks.shape[-1] == 7
+    chunks[0, 0, -1] = 64          # include the ragged last chunk once
+    chunks[0, 0] = np.sort(chunks[0, 0])
+    if len(set(chunks[0, 0].tolist())) < 7:
+        chunks[0, 0] = np.array([1, 5, 9, 20, 33, 50, 64], dtype=np.int32)
+    check_block(w, prefix, blocks[0], r, "cached", chunks=chunks)
+
+
+@pytest.mark.parametrize("r,mode", [(1, "cached"), (4, "cached"), (1, "full")])
+def test_video_frame_block(r, mode):
+    w = wl.ci_version(wl.WORKLOADS["video_1560"], prefix_len=3120, hq=4, hkv=4, n_blocks=1)
+    prefix, blocks = wl.make_inputs(w)
+    check_block(w, prefix, blocks[0], r, mode)
+
+
+def test_video_growing_prefix():
+    """Two blocks; the finalised block's last-step K/V joins the prefix."""
+    w = wl.ci_version(wl.WORKLOADS["video_1560"], prefix_len=1560, hq=2, hkv=2, n_blocks=2)
+    prefix, blocks = wl.make_inputs(w)
+    kp, vp, off = prefix.k, prefix.v, prefix.offsets
+    for bi, blk in enumerate(blocks):
+        p = wl.Prefix(kp, vp, off)
+        check_block(w, p, blk, 4, "cached")
+        kp, vp, off = oracle.grow_prefix(kp, vp, off, blk.k[-1], blk.v[-1])
+    assert off[-1] == 1560 * 3
+
+
+@pytest.mark.parametrize("r,mode", [(1, "cached"), (2, "cached"), (8, "cached"), (1, "full")])
+def test_batched_ragged(r, mode):
+    w = wl.ci_version(wl.WORKLOADS["batched_64k"], prefix_len=1000)
+    prefix, blocks = wl.make_inputs(w)
+    assert len(set(prefix.lengths)) > 1
+    check_block(w, prefix, blocks[0], r, mode)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _custom(dtype, batch, hq, hkv, d, lb, lens, steps=2, seed=99):
+    w = wl.Workload("edge", dtype, batch, hq, hkv, d, lb, 0, steps, 1.0, 0.1, seed=seed)
+    rng = np.random.default_rng(seed)
+    off = np.zeros(batch + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens)
+    t = int(off[-1])
+    draw = (lambda s: wl.round_bf16(rng.standard_normal(s, dtype=np.float32))) if dtype == "bf16" else \
+        (lambda s: rng.standard_normal(s, dtype=np.float32))
+    prefix = wl.Prefix(draw((t, hkv, d)), draw((t, hkv, d)), off)
+    blk = wl.make_block_steps(w, rng)
+    return w, prefix, blk
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", [
+    dict(batch=2, hq=4, hkv=2, d=128, lb=8, lens=[0, 0]),          # empty prefix everywhere
+    dict(batch=3, hq=4, hkv=2, d=128, lb=8, lens=[10, 0, 70]),     # < 1 tile, empty, ragged
+    dict(batch=1, hq=1, hkv=1, d=128, lb=1, lens=[129]),           # single query row
+    dict(batch=1, hq=8, hkv=2, d=64, lb=17, lens=[300]),           # D=64, G=4, 68 rows per KV head
+    dict(batch=1, hq=2, hkv=1, d=128, lb=100, lens=[64 * 5]),      # 200 rows: several row tiles
+])
+def test_edge_shapes(dtype, case):
+    w, prefix, blk = _custom(dtype, **case)
+    for r, mode in ((1, "cached"), (2, "cached"), (1, "full")):
+        check_block(w, prefix, blk, r, mode)
+
+
+def test_r1_equals_full_bitwise_and_deterministic():
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=2000)
+    prefix, blocks = wl.make_inputs(w)
+    a = run_gpu(w, prefix, blocks[0], 1, "cached")
+    b = run_gpu(w, prefix, blocks[0], 1, "full")
+    c = run_gpu(w, prefix, blocks[0], 1, "cached")
+    for s in range(w.steps):
+        np.testing.assert_array_equal(a.out[s], b.out[s])
+        np.testing.assert_array_equal(a.out[s], c.out[s])
+        np.testing.assert_array_equal(a.lse[s], c.lse[s])
+
+
+def test_drift_parity():
+    w = wl.ci_version(wl.WORKLOADS["text_mha_4k"], prefix_len=2048)
+    prefix, blocks = wl.make_inputs(w)
+    blk = blocks[0]
+    scale = scale_of(w)
+    ref_c = oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=8)
+    ref_f = oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, mode="full")
+    got_c = run_gpu(w, prefix, blk, 8, "cached")
+    got_f = run_gpu(w, prefix, blk, 1, "full")
+    for s in range(w.steps):
+        d_ref = np.abs(ref_c.out[s] - ref_f.out[s]).max()
+        d_gpu = np.abs(got_c.out[s] - got_f.out[s]).max()
+        assert abs(d_gpu - d_ref) <= 2 * 2e-2
+        if s == 0:
+            assert d_gpu == 0.0
+
+
+def test_fb_merge_matches_oracle():
+    rng = np.random.default_rng(5)
+    rows, d = 1000, 128
+    oa, ob = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    la, lb = rng.standard_normal(rows) * 3, rng.standard_normal(rows) * 3
+    la[:10] = -np.inf
+    lb[5:15] = -np.inf
+    oa[:10] = 0
+    ob[5:15] = 0
+    ref_o, ref_l = oracle.merge(oa, la, ob, lb)
+    t = [torch.tensor(x, dtype=torch.float32, device="cuda") for x in (oa, la, ob, lb)]
+    o = torch.empty_like(t[0])
+    l = torch.empty_like(t[1])
+    fbl.fb_merge(rows, d, t[0], t[1], t[2], t[3], o, l)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o.cpu().numpy(), ref_o, rtol=0, atol=1e-5)
+    got_l = l.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(got_l[fin], ref_l[fin], rtol=0, atol=1e-5)
+    # in place: o aliases o_a, lse aliases lse_a
+    fbl.fb_merge(rows, d, t[0], t[1], t[2], t[3], t[0], t[1])
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(t[0].cpu().numpy(), ref_o, rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: the GPU runs everything, the oracle checks sampled heads
+# ---------------------------------------------------------------------------
+
+def _sampled_check(w, prefix, blk, heads, steps=(0,), r=1):
+    """Runs the whole workload on the GPU; the oracle recomputes the listed
+    (stream, query head) pairs one by one as single-head problems."""
+    scale = scale_of(w)
+    n = max(steps) + 1
+    sub = wl.BlockSteps(blk.q[:n], blk.k[:n], blk.v[:n])
+    got = run_gpu(w, prefix, sub, r, "cached")
+    for (b, h) in heads:
+        g = h // (w.hq // w.hkv)
+        t0, t1 = int(prefix.offsets[b]), int(prefix.offsets[b + 1])
+        ref = oracle.run_block(prefix.k[t0:t1, g:g + 1, :], prefix.v[t0:t1, g:g + 1, :],
+                               np.array([0, t1 - t0]), sub.q[:, b:b + 1, :, h:h + 1, :],
+                               sub.k[:, b:b + 1, :, g:g + 1, :], sub.v[:, b:b + 1, :, g:g + 1, :],
+                               scale, r=r)
+        for s in steps:
+            err = np.abs(got.out[s][b, :, h, :] - ref.out[s][0, :, 0, :]).max()
+            assert err <= 2e-2, f"stream {b} head {h} step {s}: {err:.3e}"
+            lerr = np.abs(got.lse[s][b, h] - ref.lse[s][0, 0]).max()
+            assert lerr <= 2e-2, f"stream {b} head {h} step {s}: LSE {lerr:.3e}"
+
+
+@pytest.mark.slow
+def test_full_size_text_gqa_128k():
+    w = wl.WORKLOADS["text_gqa_128k"]
+    prefix, blocks = wl.make_inputs(w)
+    _sampled_check(w, prefix, blocks[0], heads=[(0, 0), (0, 13), (0, 31)])
+
+
+@pytest.mark.slow
+def test_full_size_batched_64k():
+    w = wl.WORKLOADS["batched_64k"]
+    prefix, blocks = wl.make_inputs(w)
+    _sampled_check(w, prefix, blocks[0], heads=[(0, 0), (3, 17), (7, 31)])
+
+
+@pytest.mark.slow
+def test_full_size_text_mha_32k():
+    w = wl.WORKLOADS["text_mha_32k"]
+    prefix, blocks = wl.make_inputs(w)
+    _sampled_check(w, prefix, blocks[0], heads=[(0, 0), (0, 31)], steps=(0, 3), r=8)
+
+
+@pytest.mark.slow
+def test_full_size_video():
+    w = wl.WORKLOADS["video_1560"]
+    prefix, blocks = wl.make_inputs(wl.ci_version(w, prefix_len=w.prefix_len, n_blocks=1))
+    _sampled_check(w, prefix, blocks[0], heads=[(0, 0), (0, 11)])
