@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashBlock attention step on one MI355X.
+
+One bench step is one block of S denoising steps of one attention layer, all
+batch streams and heads: the refresh step runs the split-KV prefix pass, the
+split combine into the fp32 cache, and the fused in-block attention + LSE
+merge; the other steps run only the fused in-block + merge kernel.  Inputs
+(prefix KV cache, every step's block Q/K/V) are resident in HBM before the
+timed region; consecutive bench steps rotate over three copies of the prefix
+KV cache (like consecutive layers), so no pass finds the prefix in the 256 MB
+Infinity Cache.
+
+value = query tokens per second in cached mode with refresh period r
+      = B * Lb * S * n_blocks / (time of one bench step).
+The same line reports full recompute (the standard per-step attention over the
+whole KV cache), the cached-vs-full speedup, per-step latencies, the
+cached-vs-recompute drift, the prefix kernel against the HBM roofline, and the
+fp64 oracle timed on the host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--r R]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn-step latency & query-tok/s, cached vs full recompute; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+N_LAYERS = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, lens, sparse_tokens=None):
+    """Algorithmic bytes / flops of the prefix pass and of the in-block + merge pass."""
+    e = 2 if w.dtype == "bf16" else 4
+    tok = sum(lens) if sparse_tokens is None else sparse_tokens
+    prefix_bytes = (2 * tok * w.hkv * w.head_dim * e + w.batch * w.block_len * w.hq * w.head_dim * e
+                    + w.batch * w.hq * w.block_len * (w.head_dim + 1) * 4)
+    prefix_flops = 4 * w.hq * w.block_len * w.head_dim * tok
+    block_bytes = (w.batch * w.block_len * w.head_dim * e * (w.hq + 2 * w.hkv)
+                   + w.batch * w.hq * w.block_len * (w.head_dim + 1) * 4
+                   + w.batch * w.block_len * w.hq * w.head_dim * e)
+    block_flops = 4 * w.batch * w.hq * w.block_len ** 2 * w.head_dim
+    return prefix_bytes, prefix_flops, block_bytes, block_flops
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def cpu_baseline(w, prefix, blocks, r, budget_s=12.0):
+    """The fp64 oracle (as it stands) on the same workload's first block in
+    cached mode, on the host cores; repeated until ~budget_s of CPU work."""
+    import oracle
+    scale = 1.0 / math.sqrt(w.head_dim)
+    blk = blocks[0]
+    # bound the sample: whole streams and query heads of one block, cut down to
+    # fit the budget; the rate is per query token, so it scales linearly
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 20:
+            break
+    per_block = el / runs
+    tok = w.batch * w.block_len * w.steps
+    return {
+        "value": tok / per_block,
+        "unit": "query-tok/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{runs} x first block of {w.name} ({w.steps} steps, r={r}, all streams and heads), "
+                  f"numpy fp64, {el:.1f} s; BLAS threads as cores, elementwise single-threaded",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30, help="timed bench steps (blocks)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="text_mha_32k")
+    ap.add_argument("--r", type=int, default=8)
+    ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
+                    help="prefix KV cache layout: head-major [Hkv][T][D] or token-major [T][Hkv][D]")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (to scale FETCH_SIZE / WRITE_SIZE "
+                         "counters) and exit")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU (asked for {max(args.gpus, world)}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from cached_attention_amd import flashblock as fbl
+    from cached_attention_amd import workloads as wl
+    from cached_attention_amd.session import AttentionStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    fbl.lib()   # fails loudly when the HIP library is not built
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return 0
+    w = wl.WORKLOADS[args.workload]
+    r = args.r
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log(f"[bench] workload {w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} D={w.head_dim} Lb={w.block_len} "
+        f"Lp={w.prefix_len} S={w.steps} blocks={w.n_blocks} r={r}")
+    t_gen = time.perf_counter()
+    prefix, blocks = wl.make_inputs(w)
+    log(f"[bench] inputs drawn in {time.perf_counter() - t_gen:.1f} s")
+
+    # per-block prefix: blocks after the first see the earlier blocks' final K/V appended
+    block_prefix = []
+    kp_np, vp_np, off = prefix.k, prefix.v, prefix.offsets
+    for j, blk in enumerate(blocks):
+        block_prefix.append((kp_np, vp_np, off))
+        if j + 1 < len(blocks):
+            ks, vs = [], []
+            new_off = np.zeros_like(off)
+            for b in range(w.batch):
+                t0, t1 = int(off[b]), int(off[b + 1])
+                ks += [kp_np[t0:t1], blk.k[-1][b]]
+                vs += [vp_np[t0:t1], blk.v[-1][b]]
+                new_off[b + 1] = new_off[b] + (t1 - t0) + w.block_len
+            kp_np, vp_np, off = np.concatenate(ks), np.concatenate(vs), new_off
+
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", tdt)
+    head_major = args.kv_layout == "head"
+    # head-major keeps each KV head's keys contiguous: a 64-key tile is one 16 KB run
+    dev_kv = (lambda x: dev(np.transpose(x, (1, 0, 2)))) if head_major else dev
+    layers = []   # N_LAYERS copies of each block's prefix
+    pre_strides = []
+    for j in range(len(blocks)):
+        kp, vp, _ = block_prefix[j]
+        t_tot = kp.shape[0]
+        pre_strides.append((w.head_dim, t_tot * w.head_dim) if head_major else (w.hkv * w.head_dim, w.head_dim))
+        k0, v0 = dev_kv(kp), dev_kv(vp)
+        layers.append([(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(N_LAYERS - 1)])
+    steps_dev = [[(dev(b.q[s]), dev(b.k[s]), dev(b.v[s])) for s in range(w.steps)] for b in blocks]
+    states = [AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, block_prefix[j][2],
+                            pre_strides=pre_strides[j])
+              for j in range(len(blocks))]
+    torch.cuda.synchronize()
+
+    counter = [0]
+
+    def bench_step(mode, rr):
+        layer = counter[0] % N_LAYERS
+        counter[0] += 1
+        for j, st in enumerate(states):
+            kp, vp = layers[j][layer]
+            for s in range(w.steps):
+                q, k, v = steps_dev[j][s]
+                st.step(q, k, v, kp, vp, s, rr, mode, want_lse=False)
+
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n   # ms
+
+    # ---- whole bench steps: cached (r) and full recompute ----
+    for _ in range(args.warmup):
+        bench_step("cached", r)
+    ms_cached = timed(lambda: bench_step("cached", r), args.steps)
+    for _ in range(max(1, args.warmup // 2)):
+        bench_step("full", 1)
+    ms_full = timed(lambda: bench_step("full", 1), args.steps)
+    q_tokens = w.batch * w.block_len * w.steps * len(blocks)
+
+    # ---- per-step latency: refresh vs reuse steps (first block) ----
+    st0 = states[0]
+    lat = {"refresh": [], "reuse": []}
+    for rep in range(max(5, args.steps // 2)):
+        kp, vp = layers[0][rep % N_LAYERS]
+        for s in range(w.steps):
+            q, k, v = steps_dev[0][s]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            refreshed = st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+            e1.record()
+            torch.cuda.synchronize()
+            lat["refresh" if refreshed else "reuse"].append(e0.elapsed_time(e1) * 1e3)
+    med = lambda xs: float(np.median(xs)) if xs else None
+
+    # ---- the dominant kernel alone: split-KV prefix pass (fb_prefix_partials) ----
+    q0 = steps_dev[0][0][0]
+    n_k = max(20, args.steps)
+    rot = [0]
+
+    def prefix_kernel():
+        kp, vp = layers[0][rot[0] % N_LAYERS]
+        rot[0] += 1
+        fbl.fb_prefix_partials(st0.desc, q0, kp, vp, None, st0.ws, st0.ws_bytes)
+
+    for _ in range(3):
+        prefix_kernel()
+    ms_prefix_kernel = timed(prefix_kernel, n_k)
+    ms_combine = timed(lambda: fbl.fb_prefix_combine(st0.desc, None, None, None, st0.o_ext, st0.lse_ext,
+                                                     st0.ws, st0.ws_bytes), n_k)
+    qb, kb, vb = steps_dev[0][1]
+    ms_block = timed(lambda: fbl.fb_block_attn(st0.desc, qb, kb, vb, st0.o_ext, st0.lse_ext, st0.o), n_k)
+    tiny = torch.zeros(8, 128, device="cuda")
+    tiny_l = torch.zeros(8, device="cuda")
+    ms_floor = timed(lambda: fbl.fb_merge(4, 128, tiny, tiny_l, tiny, tiny_l, tiny, tiny_l), 200)
+
+    # ---- drift: cached (r) vs full recompute, same inputs, first block ----
+    kp, vp = layers[0][0]
+    drift = []
+    full_o = []
+    for s in range(w.steps):
+        q, k, v = steps_dev[0][s]
+        st0.step(q, k, v, kp, vp, s, 1, "full", want_lse=False)
+        full_o.append(st0.o.float().clone())
+    for s in range(w.steps):
+        q, k, v = steps_dev[0][s]
+        st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+        drift.append(float((st0.o.float() - full_o[s]).abs().max()))
+
+    lens = block_prefix[0][2]
+    lens = [int(lens[b + 1] - lens[b]) for b in range(w.batch)]
+    pb, pf, bb, bf = algorithmic(w, lens)
+    prefix_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
+    prefix_tflops = pf / (ms_prefix_kernel * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": q_tokens / (ms_cached * 1e-3),
+        "unit": "query-tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_cached,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) draws, bf16-rounded, block random walk)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
+            "block_len": w.block_len, "prefix_len": lens if w.batch > 1 else lens[0],
+            "denoise_steps": w.steps, "blocks": len(blocks), "refresh_period": r,
+            "kv_layout": "head-major [Hkv][T][D]" if head_major else "token-major [T][Hkv][D]",
+            "step": "one block of denoise_steps attention steps, one layer",
+        },
+        "full_recompute": {"value": q_tokens / (ms_full * 1e-3), "unit": "query-tok/s", "ms_per_step": ms_full},
+        "speedup_vs_full": ms_full / ms_cached,
+        "step_latency_us": {"refresh_median": med(lat["refresh"]), "reuse_median": med(lat["reuse"]),
+                            "launch_floor": ms_floor * 1e3},
+        "kernels_us": {"prefix_splitkv": ms_prefix_kernel * 1e3, "split_combine": ms_combine * 1e3,
+                       "block_attn_merge": ms_block * 1e3},
+        "drift_max_abs": max(drift),
+        "drift_per_step": drift,
+        "roofline": {
+            "bound": "hbm", "achieved": prefix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": prefix_gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials)",
+            "algorithmic_bytes_per_launch": pb,
+            "mfma_tflops": prefix_tflops, "mfma_frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(w, wl.Prefix(*block_prefix[0]), blocks, r)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

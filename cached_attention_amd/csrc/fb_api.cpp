@@ -40,21 +40,29 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int esize(const fb_desc* d) { return d->dtype == FB_BF16 ? 2 : 4; }
 
-// Query rows per workgroup for the prefix pass (bf16: 64 * qt).
-int prefix_qt(const fb_desc* d) {
+// Kernel configuration of each pass, by query rows per KV head (G * Lb).
+int prefix_cfg(const fb_desc* d) {
   const int rows = (d->hq / d->hkv) * d->block_len;
-  if (d->dtype == FB_F32) return 1;
-  return rows <= 64 ? 1 : rows <= 128 ? 2 : 4;
+#if defined(FB_PREFIX_CFG_32) && defined(FB_PREFIX_CFG_64) && defined(FB_PREFIX_CFG_128) && defined(FB_PREFIX_CFG_256)
+  // build-time override of the per-size choice (used to sweep configurations)
+  return rows <= 32 ? FB_PREFIX_CFG_32 : rows <= 64 ? FB_PREFIX_CFG_64 : rows <= 128 ? FB_PREFIX_CFG_128
+                                                                                     : FB_PREFIX_CFG_256;
+#else
+  // measured on MI355X: two independent workgroups per CU for up to 128 rows
+  // (their waves drift apart, so one's softmax overlaps the other's MFMAs);
+  // the eight-wave ping-pong workgroup for 256 rows
+  return rows <= 32 ? fb::CFG_P32_X2 : rows <= 64 ? fb::CFG_P64_X2 : rows <= 128 ? fb::CFG_P128_X2
+                                                                                 : fb::CFG_P256_PP;
+#endif
 }
-int block_qt(const fb_desc* d) {
+int block_cfg(const fb_desc* d) {
   const int rows = (d->hq / d->hkv) * d->block_len;
-  if (d->dtype == FB_F32) return 1;
-  return rows >= 512 ? 2 : 1;
+  return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B64;
 }
-// Workgroups resident per CU for a given row tile (register / LDS limits).
-int wgs_per_cu(const fb_desc* d, int qt) {
-  if (d->dtype == FB_F32) return 2;
-  return qt >= 2 ? 1 : 2;
+// fp32 inputs run the VALU kernel: 64 rows per workgroup, 2 per CU.
+fb::CfgInfo pass_info(const fb_desc* d, int cfg) {
+  if (d->dtype == FB_F32) return {64, 2};
+  return fb::cfg_info(cfg);
 }
 
 fb_status check_desc(const fb_desc* d) {
@@ -81,6 +89,9 @@ fb_status check_desc(const fb_desc* d) {
     if ((s * e) % 16 != 0)
       return fail(FB_ERR_ALIGN, "stride %lld elements is not a multiple of 16 bytes", (long long)s);
   }
+  // a 64-key tile's row offsets are kept in 31 bits by the kernels
+  if (d->kv_stride_t * e * 64 >= (1LL << 31) || d->pre_stride_t * e * 64 >= (1LL << 31))
+    return fail(FB_ERR_SHAPE, "token stride too large");
   return FB_OK;
 }
 
@@ -117,7 +128,7 @@ fb_status check_sparse(const fb_sparse* sp, bool need_mode) {
 // ---------------------------------------------------------------------------
 
 struct PrefixPlan {
-  int qt, row_tiles, split_tiles, total_splits, n_work, grid;
+  int cfg, row_tiles, split_tiles, total_splits, n_work, grid;
   int chunk_mode, n_sel, chunk_tiles;
   size_t part_o_bytes, part_lse_bytes;
 };
@@ -130,17 +141,30 @@ int64_t logical_tiles_host(const fb_desc* d, int b, int chunk_mode, int n_sel, i
 
 fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len, PrefixPlan* p) {
   const int rows = (d->hq / d->hkv) * d->block_len;
-  p->qt = prefix_qt(d);
-  const int rows_per_wg = d->dtype == FB_F32 ? 64 : 64 * p->qt;
-  p->row_tiles = (int)ceil_div(rows, rows_per_wg);
+  p->cfg = prefix_cfg(d);
+  const fb::CfgInfo ci = pass_info(d, p->cfg);
+  p->row_tiles = (int)ceil_div(rows, ci.rows);
   p->chunk_mode = chunk_mode;
   p->n_sel = n_sel;
   p->chunk_tiles = chunk_mode == fb::CHUNKS_ALL ? 1 : chunk_len / fb::kTile;
   const int64_t units = (int64_t)d->hkv * p->row_tiles;
   int64_t total_tiles = 0;
   for (int b = 0; b < d->batch; ++b) total_tiles += logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles);
-  const int64_t target = (int64_t)kCUs * wgs_per_cu(d, p->qt);
-  int64_t st = std::max<int64_t>(kMinSplitTiles, ceil_div(total_tiles * units, target));
+  // Smallest split length whose workgroups all fit in one resident round
+  // (capacity = CUs x workgroups per CU): a second, partly filled round would
+  // double the pass time.  Splits of at least kMinSplitTiles tiles.
+  const int64_t capacity = (int64_t)kCUs * ci.wgs_per_cu;
+  int64_t max_tiles = 0;
+  for (int b = 0; b < d->batch; ++b)
+    max_tiles = std::max(max_tiles, logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles));
+  auto wgs_for = [&](int64_t st_) {
+    int64_t n = 0;
+    for (int b = 0; b < d->batch; ++b) n += ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles), st_);
+    return n * units;
+  };
+  int64_t st = std::max<int64_t>(kMinSplitTiles, ceil_div(total_tiles * units, capacity));
+  while (st < max_tiles && wgs_for(st) > capacity) ++st;
+  st = std::max<int64_t>(st, kMinSplitTiles);
   if (st > (1 << 28)) st = 1 << 28;
   p->split_tiles = (int)st;
   int64_t splits = 0;
@@ -182,20 +206,16 @@ fb_status hip_status(int err, const char* what) {
   return FB_OK;
 }
 
-// Prefix pass with a chosen chunk mode; `extra_*` (nullable) is one more
-// partial folded into the combine (the sparse residual).
-fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
-                     const fb_sparse* sp, const float* extra_o, const float* extra_lse, float* o_ext,
-                     float* lse_ext, void* ws, size_t ws_bytes, void* stream) {
+// The two halves of the prefix pass for a chosen chunk mode.  Both derive the
+// same plan (and so the same workspace layout) from (d, chunk mode, sp).
+fb_status run_partials(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
+                       const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream) {
   PrefixPlan p;
   const int n_sel = sp ? sp->k : 0;
-  const int chunk_len = sp ? sp->chunk_len : 64;
-  fb_status st = plan_prefix(d, chunk_mode, n_sel, chunk_len, &p);
+  fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
   if (st != FB_OK) return st;
   if (p.part_o_bytes + p.part_lse_bytes > ws_bytes)
     return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.part_o_bytes + p.part_lse_bytes);
-  float* part_o = (float*)ws;
-  float* part_lse = (float*)((char*)ws + p.part_o_bytes);
   fb::AttnArgs a;
   fill_common(d, q, &a);
   a.k = k_pre;
@@ -211,14 +231,24 @@ fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const v
   a.n_sel = n_sel;
   a.chunk_tiles = p.chunk_tiles;
   a.chunk_mode = chunk_mode;
-  a.part_o = part_o;
-  a.part_lse = part_lse;
-  st = hip_status(fb::launch_attn(a, d->dtype, d->head_dim, p.qt, true, stream), "prefix attention launch");
+  a.part_o = (float*)ws;
+  a.part_lse = (float*)((char*)ws + p.part_o_bytes);
+  return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, p.cfg, true, stream), "prefix attention launch");
+}
+
+fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, const float* extra_o,
+                      const float* extra_lse, float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes,
+                      void* stream) {
+  PrefixPlan p;
+  const int n_sel = sp ? sp->k : 0;
+  fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
   if (st != FB_OK) return st;
+  if (p.part_o_bytes + p.part_lse_bytes > ws_bytes)
+    return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, p.part_o_bytes + p.part_lse_bytes);
   fb::CombineArgs c;
   memset(&c, 0, sizeof(c));
-  c.part_o = part_o;
-  c.part_lse = part_lse;
+  c.part_o = (const float*)ws;
+  c.part_lse = (const float*)((const char*)ws + p.part_o_bytes);
   c.offsets = d->prefix_offsets_dev;
   c.B = d->batch;
   c.Hq = d->hq;
@@ -237,6 +267,14 @@ fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const v
   return hip_status(fb::launch_combine(c, rows, stream), "split combine launch");
 }
 
+fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
+                     const fb_sparse* sp, const float* extra_o, const float* extra_lse, float* o_ext,
+                     float* lse_ext, void* ws, size_t ws_bytes, void* stream) {
+  fb_status st = run_partials(d, q, k_pre, v_pre, chunk_mode, sp, ws, ws_bytes, stream);
+  if (st != FB_OK) return st;
+  return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream);
+}
+
 fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const void* v_blk, const float* o_ext,
                     const float* lse_ext, void* o, float* lse_out, void* stream) {
   fb::AttnArgs a;
@@ -247,9 +285,8 @@ fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const vo
   a.kv_st = d->kv_stride_t;
   a.kv_sh = d->kv_stride_h;
   a.offsets = nullptr;
-  const int qt = block_qt(d);
-  const int rows_per_wg = d->dtype == FB_F32 ? 64 : 64 * qt;
-  a.row_tiles = (int)ceil_div(a.rows, rows_per_wg);
+  const int cfg = block_cfg(d);
+  a.row_tiles = (int)ceil_div(a.rows, pass_info(d, cfg).rows);
   a.split_tiles = (int)ceil_div(d->block_len, fb::kTile);
   const int64_t work = (int64_t)d->batch * d->hkv * a.row_tiles;
   if (work > (1LL << 30)) return fail(FB_ERR_SHAPE, "block pass needs too many workgroups");
@@ -259,7 +296,7 @@ fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const vo
   a.ext_lse = lse_ext;
   a.o = o;
   a.lse_out = lse_out;
-  return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, qt, false, stream), "block attention launch");
+  return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, cfg, false, stream), "block attention launch");
 }
 
 size_t workspace_for(const fb_desc* d, const fb_sparse* sp) {
@@ -330,6 +367,39 @@ fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre,
   if (st != FB_OK) return st;
   const int mode = sp ? sp->mode : fb::CHUNKS_ALL;
   return run_prefix(d, q_blk, k_pre, v_pre, mode, sp, nullptr, nullptr, o_ext, lse_ext, ws, ws_bytes, stream);
+}
+
+fb_status fb_prefix_partials(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
+                             const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st != FB_OK) return st;
+  if (!q_blk) return fail(FB_ERR_NULL, "q_blk is required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre))
+    return fail(FB_ERR_ALIGN, "q_blk, k_pre and v_pre must be 16-byte aligned");
+  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
+  if (st != FB_OK) return st;
+  return run_partials(d, q_blk, k_pre, v_pre, sp ? sp->mode : fb::CHUNKS_ALL, sp, ws, ws_bytes, stream);
+}
+
+fb_status fb_prefix_combine(const fb_desc* d, const fb_sparse* sp, const float* extra_o, const float* extra_lse,
+                            float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st != FB_OK) return st;
+  if (!o_ext || !lse_ext) return fail(FB_ERR_NULL, "o_ext and lse_ext are required");
+  if ((extra_o == nullptr) != (extra_lse == nullptr))
+    return fail(FB_ERR_NULL, "extra_o and extra_lse must be both given or both NULL");
+  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
+  if (st != FB_OK) return st;
+  return run_combine(d, sp ? sp->mode : fb::CHUNKS_ALL, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes,
+                     stream);
 }
 
 fb_status fb_block_attn(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,

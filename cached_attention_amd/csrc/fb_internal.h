@@ -9,9 +9,55 @@ enum ChunkMode : int32_t { CHUNKS_ALL = 0, CHUNKS_SELECTED = 1, CHUNKS_COMPLEMEN
 
 constexpr int kTile = 64;  // keys per LDS tile
 
-// One attention pass: rows of query heads over a key range, either the packed
-// ragged prefix (offsets != nullptr; split over tiles) or each stream's own
-// block (offsets == nullptr; one split per stream covering its Lb keys).
+// bf16 kernel configurations.  X(id, rows per wave / 16, waves, LDS stages,
+// ping-pong schedule, resident workgroups per CU, pass: 1 = split partial of
+// the prefix pass, 0 = block pass with merge).  Query rows per workgroup =
+// waves * 16 * (rows per wave / 16).
+#define FB_BF16_CFGS(X)                                                       \
+  X(0, 1, 2, 4, false, 1, 1)   /* prefix  32 rows: 2 waves x 16          */ \
+  X(1, 1, 4, 4, false, 1, 1)   /* prefix  64 rows: 4 waves x 16          */ \
+  X(2, 2, 4, 4, false, 1, 1)   /* prefix 128 rows: 4 waves x 32          */ \
+  X(3, 2, 8, 4, false, 1, 1)   /* prefix 256 rows: 8 waves x 32          */ \
+  X(4, 1, 4, 2, false, 2, 0)   /* block   64 rows                        */ \
+  X(5, 1, 8, 2, false, 1, 0)   /* block  128 rows                        */ \
+  X(6, 2, 8, 4, true, 1, 1)    /* prefix 256 rows, ping-pong             */ \
+  X(7, 2, 4, 2, false, 2, 1)   /* prefix 128 rows, 2 workgroups per CU   */ \
+  X(8, 4, 4, 4, false, 1, 1)   /* prefix 256 rows: 4 waves x 64          */ \
+  X(9, 1, 2, 2, false, 2, 1)   /* prefix  32 rows, 2 workgroups per CU   */ \
+  X(10, 1, 4, 2, false, 2, 1)  /* prefix  64 rows, 2 workgroups per CU   */ \
+  X(11, 1, 8, 4, true, 1, 1)   /* prefix 128 rows: 8 waves x 16, ping-pong */ \
+  X(12, 1, 8, 4, false, 1, 1)  /* prefix 128 rows: 8 waves x 16          */
+
+enum KernelCfg : int32_t {
+  CFG_P32 = 0,
+  CFG_P64 = 1,
+  CFG_P128 = 2,
+  CFG_P256 = 3,
+  CFG_B64 = 4,
+  CFG_B128 = 5,
+  CFG_P256_PP = 6,
+  CFG_P128_X2 = 7,
+  CFG_P256_Q4 = 8,
+  CFG_P32_X2 = 9,
+  CFG_P64_X2 = 10,
+  CFG_P128_W8PP = 11,
+  CFG_P128_W8 = 12,
+};
+
+struct CfgInfo {
+  int rows;         // query rows per workgroup
+  int wgs_per_cu;   // resident workgroups per CU (LDS / register bound)
+};
+inline CfgInfo cfg_info(int cfg) {
+  switch (cfg) {
+#define FB_CFG_INFO(ID, QT, NW, NS, PP, WPC, PART) \
+    case ID: return {(NW) * 16 * (QT), WPC};
+    FB_BF16_CFGS(FB_CFG_INFO)
+#undef FB_CFG_INFO
+    default: return {64, 1};
+  }
+}
+
 struct AttnArgs {
   // queries [B][Lb][Hq][D] with element strides
   const void* q;
@@ -55,7 +101,7 @@ struct CombineArgs {
 };
 
 // launchers (fb_kernels.hip); return hipError_t as int
-int launch_attn(const AttnArgs& a, int dtype, int head_dim, int qt, bool partial, void* stream);
+int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partial, void* stream);
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream);
 int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* la, const float* ob,
                  const float* lb, float* o, float* lse, void* stream);

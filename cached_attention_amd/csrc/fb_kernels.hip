@@ -46,11 +46,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Read-only kernel inputs (offsets, chunk lists) are read through the constant
+// address space: wave-uniform loads then become scalar loads, which do not
+// count against vmcnt and so never stall the direct-to-LDS pipeline.
+#define FB_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const FB_CONST T*)p)[i];
+}
+
 // ---------------------------------------------------------------------------
 // Split plan, evaluated identically by the attention and combine kernels.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int64_t prefix_len(const int64_t* off, int b) { return off[b + 1] - off[b]; }
+__device__ __forceinline__ int64_t prefix_len(const int64_t* off, int b) {
+  return ld_const(off, b + 1) - ld_const(off, b);
+}
 
 // Logical tiles of stream b: SELECTED walks the listed chunks, otherwise the
 // prefix positions (COMPLEMENT skips listed chunks while walking).
@@ -82,15 +93,15 @@ __device__ __forceinline__ bool next_tile(TileIter& it, int64_t& tok0, int& nval
     const int i = it.lt++;
     int64_t start;
     if (it.mode == CHUNKS_SELECTED) {
-      const int64_t c = it.list[i / it.ct];
+      const int64_t c = ld_const(it.list, i / it.ct);
       start = (c * it.ct + (i % it.ct)) * (int64_t)kTile;
       if (c < 0 || start >= it.lp) continue;
     } else {
       start = (int64_t)i * kTile;
       if (it.mode == CHUNKS_COMPLEMENT) {
         const int c = i / it.ct;
-        while (it.ptr < it.nlist && it.list[it.ptr] < c) ++it.ptr;
-        if (it.ptr < it.nlist && it.list[it.ptr] == c) continue;
+        while (it.ptr < it.nlist && ld_const(it.list, it.ptr) < c) ++it.ptr;
+        if (it.ptr < it.nlist && ld_const(it.list, it.ptr) == c) continue;
       }
     }
     tok0 = start;
@@ -156,12 +167,12 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
         int lo = 0, hi = it.nlist;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
-          if (it.list[mid] < c0) lo = mid + 1; else hi = mid;
+          if (ld_const(it.list, mid) < c0) lo = mid + 1; else hi = mid;
         }
         it.ptr = lo;
       }
     }
-    tok_base = a.offsets[b];
+    tok_base = ld_const(a.offsets, b);
     wk.kbase = (const char*)a.k + (tok_base * a.kv_st + (int64_t)wk.g * a.kv_sh) * ESZ;
     wk.vbase = (const char*)a.v + (tok_base * a.kv_st + (int64_t)wk.g * a.kv_sh) * ESZ;
   } else {
@@ -179,29 +190,140 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 // bf16 attention on MFMA
 // ---------------------------------------------------------------------------
 //
-// Workgroup: 4 waves; wave w owns 16*QT consecutive query rows of one KV head
+// Workgroup: NW waves; wave w owns 16*QT consecutive query rows of one KV head
 // (row i -> query head g*G + i / Lb, block position i % Lb).  Per 64-key tile:
 //   S^T[key][q] = K Q^T      v_mfma_f32_16x16x32_bf16, A = K from LDS,
 //                            B = Q^T held in VGPRs for the whole pass
 //   online softmax on S^T    each lane holds one query column (lane & 15) and
 //                            16 keys of it; row max over the 4 lane groups by
 //                            two xor-shuffles; exp2 with scale*log2(e) folded in
-//   O^T[d][q] += V^T P^T     A = V^T from LDS, B = P^T straight from the score
-//                            accumulators (bf16), no cross-lane movement
-// Staging: 256 units of eight 16-byte global loads per tile (half K, half V),
-// loaded into VGPRs one tile ahead and written to the other LDS stage after
-// the current tile's MFMAs; V is transposed in registers (8x8 bf16 blocks).
+//   O^T[d][q] += V^T P^T     A = V^T read from the row-major V tile with the
+//                            LDS transpose read, B = P^T straight from the
+//                            score accumulators (bf16), no cross-lane movement
+// Keys and values move HBM -> LDS with direct-to-LDS loads into an NS-stage
+// ring, DIST tiles ahead of the tile being computed; each wave waits only for
+// the tile it is about to read (per-stage vmcnt), then one barrier per tile.
+//
+// Eight-wave workgroups run a ping-pong schedule: waves 4..7 lag waves 0..3
+// by half a tile (they run the softmax and PV product of tile k-1 while the
+// leading waves compute the scores of tile k), so the two waves sharing a
+// SIMD are in different phases and one's VALU work overlaps the other's MFMA
+// work.  The lag keeps one extra stage in use, so these workgroups prefetch
+// NS-2 tiles ahead instead of NS-1.
+//
+// Running max: the first tile of a pass sets it from the exact row maxima;
+// later tiles compute p = exp2(s*c - m) against it directly and only fall back
+// to exact maxima plus a rescale of O and l when some row's partial sum shows
+// p beyond 2^64 (or not finite).  Every p stays far inside the fp32 / bf16
+// range and the normalised result is unchanged, while the common tile skips
+// the max reduction altogether.
 
-template <int D, int QT, bool PARTIAL>
-__global__ void __launch_bounds__(256) attn_bf16(const AttnArgs a) {
-  constexpr int KS = D / 32;            // k-steps of the score MFMA
-  constexpr int DT = D / 16;            // 16-row d tiles of O^T
-  constexpr int CH = D / 8;             // 16-byte chunks per key row
-  constexpr int ROWS = 64 * QT;         // query rows per workgroup
-  constexpr int KBYTES = kTile * D * 2;
-  constexpr int STAGE = 2 * KBYTES;
-  constexpr int HALF_UNITS = (kTile / 8) * CH;  // K units == V units
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+constexpr float kOverflowSum = 1.8446744e19f;  // 2^64: partial row sums beyond it take the exact-max path
+
+#define FB_LDS __attribute__((address_space(3)))
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
+// s_waitcnt vmcnt(n) for n = k * per, k in [0, 3] (gfx9 encoding: expcnt and
+// lgkmcnt left at their maxima)
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_tiles(int k) {
+  constexpr int base = 0x0F70;
+  switch (k) {
+    case 0: __builtin_amdgcn_s_waitcnt(base | 0); break;
+    case 1: __builtin_amdgcn_s_waitcnt(base | ((PER & 15) | ((PER >> 4) << 14))); break;
+    case 2: __builtin_amdgcn_s_waitcnt(base | (((2 * PER) & 15) | (((2 * PER) >> 4) << 14))); break;
+    default: __builtin_amdgcn_s_waitcnt(base | (((3 * PER) & 15) | (((3 * PER) >> 4) << 14))); break;
+  }
+}
+
+__device__ __forceinline__ void lds_dma_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+__device__ __forceinline__ int kv_swz(int key) {
+  // 16-byte slot XOR: even values only, so the two 16-byte slots holding one
+  // 16-dim column block stay adjacent (the transpose read fetches 8-byte
+  // halves of both)
+  return D == 128 ? ((key & 7) << 1) : ((key & 3) << 1);
+}
+
+// LDS reads of the MFMA operands are written as asm blocks that end with
+// their own lgkmcnt wait, so no read is left in flight when a block returns.
+// The compiler cannot tell these reads apart from direct-to-LDS writes still
+// in flight to other stages and would otherwise drain every outstanding load
+// before each of them.
+
+// four 16-byte reads (K fragments) at a + 0, STRIDE, 2*STRIDE, 3*STRIDE
+template <int STRIDE>
+__device__ __forceinline__ void lds_read4_rows(uint32_t a, u32x4 out[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:%5\n\t"
+      "ds_read_b128 %2, %4 offset:%6\n\t"
+      "ds_read_b128 %3, %4 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+      : "v"(a), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE)
+      : "memory");
+}
+
+// four 16-byte reads at a0..a3 + OFF
+template <int OFF>
+__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4 out[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF)
+      : "memory");
+}
+
+// four pairs of transpose reads (V^T fragment halves at +OFF and +OFF+HALF)
+template <int OFF, int HALF>
+__device__ __forceinline__ void lds_tr_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2 lo[4],
+                                             u32x2 hi[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+        "=&v"(hi[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF), "i"(OFF + HALF)
+      : "memory");
+}
+
+template <int D, int QT, int NW, int NS, bool PP, int MINW, bool PARTIAL>
+__global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
+  constexpr int KS = D / 32;                  // k-steps of the score MFMA
+  constexpr int DT = D / 16;                  // 16-row d tiles of O^T
+  constexpr int CH = D / 8;                   // 16-byte slots per key row
+  constexpr int ROWS = NW * 16 * QT;          // query rows per workgroup
+  constexpr int TBYTES = kTile * D * 2;       // one K or V tile
+  constexpr int STAGE = 2 * TBYTES;
+  constexpr int IPT = TBYTES / 1024;          // 1 KB direct-to-LDS loads per tile and tensor
+  constexpr int IPW = 2 * IPT / NW;           // loads per wave per tile
+  constexpr int RPI = 1024 / (2 * D);         // key rows per load instruction
+  constexpr int DIST = PP ? NS - 2 : NS - 1;  // prefetch distance in tiles
+  static_assert(IPT % IPW == 0 && IPW % 2 == 0, "each wave loads an even run of one tensor");
+  static_assert(NS >= 2 && NS <= 4 && DIST >= 1, "2..4 stages");
+  static_assert((DIST - 1) * IPW < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   Work wk;
   if (!decode_work<2>(a, wk)) return;
@@ -211,6 +333,8 @@ __global__ void __launch_bounds__(256) attn_bf16(const AttnArgs a) {
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  const bool lagging = PP && wave >= NW / 2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- query fragments (B operand of the score MFMA) ----
   const int row_w0 = wk.rt * ROWS + wave * 16 * QT;
@@ -244,85 +368,130 @@ __global__ void __launch_bounds__(256) attn_bf16(const AttnArgs a) {
     l_run[qt] = 0.f;
   }
 
-  // ---- staging role of this thread ----
-  const bool is_k = tid < HALF_UNITS;
-  const bool is_v = !is_k && tid < 2 * HALF_UNITS;
-  const int unit = is_k ? tid : tid - HALF_UNITS;
-  const int uc = unit % CH;   // 16-byte chunk (8 dims)
-  const int ug = unit / CH;   // group of 8 keys
-  int utok[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    if (is_k) {
-      utok[r] = ug * 8 + r;
-    } else {  // keys whose P values one lane group holds for one 32-key MFMA step
-      const int jj = ug >> 2, gq = ug & 3;
-      utok[r] = jj * 32 + (r < 4 ? 4 * gq + r : 16 + 4 * gq + (r - 4));
-    }
-  }
-  const char* gsrc = is_k ? wk.kbase : wk.vbase;
+  // ---- direct-to-LDS tile loads ----
+  // Waves 0..NW/2-1 load K, the others V; wave w's IPW instructions cover the
+  // 1 KB chunks jj0 .. jj0+IPW-1 of its tensor's tile (RPI key rows each).
+  // Lane -> (key row, 16-byte slot); the slot swizzle is applied on the global
+  // side so each instruction writes one contiguous 1 KB block of LDS.  The
+  // per-lane part of the global offset depends only on the chunk parity.
+  const bool dma_v = wave >= NW / 2;
+  const int jj0 = (dma_v ? wave - NW / 2 : wave) * IPW;
+  const char* gsrc = dma_v ? wk.vbase : wk.kbase;
+  const uint32_t lds_dst = lds0 + (dma_v ? TBYTES : 0) + jj0 * 1024;
   const int64_t row_bytes = a.kv_st * 2;
-  u32x4 stg[8];
-
-  auto stage_load = [&](int64_t tok0, int nvalid) {
-    if (!(is_k || is_v)) return;
+  uint32_t lane_part[2];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (utok[r] < nvalid)
-        stg[r] = *(const u32x4*)(gsrc + (tok0 + utok[r]) * row_bytes + uc * 16);
-      else
-        stg[r] = (u32x4){0u, 0u, 0u, 0u};
-    }
-  };
-  auto stage_store = [&](int buf) {
-    char* base = smem + buf * STAGE;
-    if (is_k) {
+  for (int par = 0; par < 2; ++par) {
+    const int row = par * RPI + lane / CH;
+    lane_part[par] = (uint32_t)(row * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16;
+  }
+  auto issue = [&](int stage, int64_t tok0, int nvalid) {
+    const char* g = gsrc + tok0 * row_bytes;
+    const uint32_t dst = lds_dst + stage * STAGE;
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        *(u32x4*)(base + (ug * 8 + r) * (D * 2) + ((uc ^ r) * 16)) = stg[r];
-    } else if (is_v) {
-      const int slot = ((ug >> 2) << 2) | (ug & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = uc * 8 + e;
-        const int dw = e >> 1;
-        u32x4 outv;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t x0 = stg[2 * kk][dw];
-          const uint32_t x1 = stg[2 * kk + 1][dw];
-          outv[kk] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        }
-        const int phys = slot ^ ((d ^ (d >> 3)) & 7);
-        *(u32x4*)(base + KBYTES + d * 128 + phys * 16) = outv;
+    for (int u = 0; u < IPW; ++u) {
+      const int jj = jj0 + u;
+      uint32_t off = lane_part[u & 1] + (uint32_t)((jj - (u & 1)) * RPI * row_bytes);
+      if (nvalid < kTile) {   // ragged tile: rows past the end re-read the last key (masked later)
+        const int row = jj * RPI + lane / CH;
+        const int srow = row < nvalid ? row : nvalid - 1;
+        off = (uint32_t)(srow * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16;
       }
+      __builtin_amdgcn_global_load_lds((const void*)(g + off), (FB_LDS void*)(uintptr_t)(dst + u * 1024), 16, 0,
+                                       0);
     }
   };
 
   const float c = a.c_log2;
+  // per-lane LDS offsets of the K fragment reads (key 16*tt + l16, 16-byte
+  // slot 4*ks + lg, swizzled) and of the V transpose reads (key 4*lg +
+  // (l16 >> 2), dims 16*dt + 4*(l16 & 3), swizzled)
+  uint32_t koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = l16 * (2 * D) + (((ks * 4 + lg) ^ kv_swz<D>(l16)) * 16);
+  const uint32_t vlane = (4 * lg + (l16 >> 2)) * (2 * D) + 8 * (l16 & 3);
+  const int vkx = kv_swz<D>(4 * lg + (l16 >> 2)) >> 1;
 
-  auto compute = [&](int buf, int nvalid) {
-    const char* Ks = smem + buf * STAGE;
-    const char* Vs = Ks + KBYTES;
-    f32x4 s[4][QT];
+  f32x4 s[4][QT];
+
+  // S^T = K Q^T for the tile at LDS offset kb; k-step outer so that the
+  // 4 x QT accumulators of a step are independent MFMA chains
+  auto scores = [&](uint32_t kb) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = tt * 16 + l16;
-      bf16x8 kf[KS];
+    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int slot = ks * 4 + lg;
-        kf[ks] = *(const bf16x8*)(Ks + tok * (D * 2) + ((slot ^ (tok & 7)) * 16));
-      }
+      for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 kraw[4];   // keys 16*tt + l16, tt = 0..3, 16-byte slot 4*ks + lg
+      lds_read4_rows<16 * 2 * D>(kb + koff[ks], kraw);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qt][ks], acc, 0, 0, 0);
-        s[tt][qt] = acc;
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw[tt]), qf[qt][ks],
+                                                              s[tt][qt], 0, 0, 0);
+    }
+  };
+
+  // exact row maxima of the tile (4 lane groups share a query column)
+  auto raise_max = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt][i]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m_run[qt], mx * c);
+      if (m_new != m_run[qt]) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);   // 0 when m_run = -inf
+        m_run[qt] = m_new;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
       }
     }
+  };
+
+  // p = exp2(s*c - m), packed to bf16 for the PV product; false if some
+  // partial row sum leaves the safe range
+  bf16x8 pf[2][QT];
+  float rs[QT];
+  auto exps = [&]() -> bool {
+    bool ok = true;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float msub = m_run[qt] == kNegInf ? 0.f : m_run[qt];
+      float sum = 0.f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][qt][i], c, -msub));
+          sum += p[i];
+        }
+        pk[tt][0] = pack_bf16x2(p[0], p[1]);
+        pk[tt][1] = pack_bf16x2(p[2], p[3]);
+      }
+      rs[qt] = sum;
+      ok &= sum <= kOverflowSum || sum != sum;   // NaN inputs propagate, no retry
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        u32x4 pv = {pk[2 * jj][0], pk[2 * jj][1], pk[2 * jj + 1][0], pk[2 * jj + 1][1]};
+        pf[jj][qt] = __builtin_bit_cast(bf16x8, pv);
+      }
+    }
+    return ok;
+  };
+
+  // softmax of the scores in s (tile with nvalid keys), then O^T += V^T P^T
+  // with V at LDS offset vb
+  auto softmax_pv = [&](uint32_t vb, int nvalid) {
     if (nvalid < kTile) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -334,76 +503,91 @@ __global__ void __launch_bounds__(256) attn_bf16(const AttnArgs a) {
             if (dead) s[tt][qt][i] = kNegInf;
         }
     }
-    bf16x8 pf[2][QT];
+    bool first = false;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = kNegInf;
+    for (int qt = 0; qt < QT; ++qt) first |= m_run[qt] == kNegInf;
+    if (__any(first)) raise_max();
+    if (!__all(exps())) {   // rare: a row's scores jumped far above the running max
+      raise_max();
+      exps();
+    }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+    for (int qt = 0; qt < QT; ++qt) l_run[qt] += rs[qt];
+    auto pv_half = [&](auto JJ) {
+      constexpr int jj = decltype(JJ)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt][i]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-      m_run[qt] = m_new;
-      float rs = 0.f;
-      uint32_t pk[4][2];
+      for (int d0 = 0; d0 < DT; d0 += 4) {
+        u32x2 lo[4], hi[4];
+        lds_tr_read4<jj * 32 * 2 * D, 16 * 2 * D>(vb + vlane + 32 * ((d0 + 0) ^ vkx), vb + vlane + 32 * ((d0 + 1) ^ vkx),
+                                                vb + vlane + 32 * ((d0 + 2) ^ vkx), vb + vlane + 32 * ((d0 + 3) ^ vkx),
+                                                lo, hi);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        float p[4];
+        for (int u = 0; u < 4; ++u) {
+          const u32x4 w = {lo[u][0], lo[u][1], hi[u][0], hi[u][1]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][qt][i], c, -m_new));
-          rs += p[i];
+          for (int qt = 0; qt < QT; ++qt)
+            oacc[d0 + u][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jj][qt], oacc[d0 + u][qt], 0, 0, 0);
         }
-        pk[tt][0] = pack_bf16x2(p[0], p[1]);
-        pk[tt][1] = pack_bf16x2(p[2], p[3]);
       }
-      l_run[qt] = l_run[qt] * alpha + rs;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        u32x4 pv = {pk[2 * jj][0], pk[2 * jj][1], pk[2 * jj + 1][0], pk[2 * jj + 1][1]};
-        pf[jj][qt] = __builtin_bit_cast(bf16x8, pv);
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 16 + l16;
-        const int slot = jj * 4 + lg;
-        const bf16x8 vf = *(const bf16x8*)(Vs + d * 128 + ((slot ^ ((d ^ (d >> 3)) & 7)) * 16));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jj][qt], oacc[dt][qt], 0, 0, 0);
-      }
-    }
+    };
+    pv_half(IC<0>{});
+    pv_half(IC<1>{});
   };
 
-  // ---- pipelined main loop: global loads of tile i+1 overlap compute of tile i ----
-  int64_t tok_cur = 0, tok_nxt = 0;
-  int nv_cur = 0, nv_nxt = 0;
-  bool have_cur = next_tile(wk.it, tok_cur, nv_cur);
-  if (have_cur) {
-    stage_load(tok_cur, nv_cur);
-    stage_store(0);
+  // ---- pipeline: position j of the queue = tile k + j; stage of tile k = st ----
+  bool q_have[4] = {false, false, false, false};
+  int64_t q_tok[4] = {0, 0, 0, 0};
+  int q_nv[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < DIST; ++j) {
+    q_have[j] = (j == 0 || q_have[j - 1]) && next_tile(wk.it, q_tok[j], q_nv[j]);
+    if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
   }
-  __syncthreads();
-  bool have_nxt = have_cur && next_tile(wk.it, tok_nxt, nv_nxt);
-  int buf = 0;
-  while (have_cur) {
-    if (have_nxt) stage_load(tok_nxt, nv_nxt);
-    if (wave_active) compute(buf, nv_cur);
-    if (have_nxt) stage_store(buf ^ 1);
-    __syncthreads();
-    have_cur = have_nxt;
-    tok_cur = tok_nxt;
-    nv_cur = nv_nxt;
-    buf ^= 1;
-    if (have_cur) have_nxt = next_tile(wk.it, tok_nxt, nv_nxt);
+  int st = 0;
+  bool prev_ok = false;      // ping-pong lagging waves: scores of the previous tile wait in s
+  int prev_nv = 0;
+  uint32_t prev_vb = 0;
+  for (;;) {
+    const bool cur = q_have[0];
+    if (!cur && !(PP && lagging && prev_ok)) break;
+    auto sync_issue = [&]() {
+      int after = 0;
+#pragma unroll
+      for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
+      wait_vmcnt_tiles<IPW>(after);
+      lds_dma_barrier();
+      q_have[DIST] = q_have[DIST - 1] && next_tile(wk.it, q_tok[DIST], q_nv[DIST]);
+      if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
+    };
+    const uint32_t kb = lds0 + st * STAGE;
+    if constexpr (!PP) {
+      sync_issue();
+      if (wave_active) {
+        scores(kb);
+        softmax_pv(kb + TBYTES, q_nv[0]);
+      }
+    } else {
+      if (cur && lagging) sync_issue();
+      if (wave_active && prev_ok) softmax_pv(prev_vb, prev_nv);
+      if (!cur) break;          // that was the last tile's softmax
+      if (!lagging) sync_issue();
+      if (wave_active) scores(kb);
+      prev_ok = true;
+      prev_nv = q_nv[0];
+      prev_vb = kb + TBYTES;
+    }
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) {
+      q_have[j] = q_have[j + 1];
+      q_tok[j] = q_tok[j + 1];
+      q_nv[j] = q_nv[j + 1];
+    }
+    q_have[DIST] = false;
+    st = st + 1 == NS ? 0 : st + 1;
+  }
+  if constexpr (PP) {
+    if (!lagging && wave_active && prev_ok) softmax_pv(prev_vb, prev_nv);
   }
 
   if (!wave_active) return;
@@ -558,22 +742,51 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64
   int ns = splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
   if (x0 > c.total_splits) x0 = c.total_splits;
   if (ns > c.total_splits - x0) ns = c.total_splits - x0;
-  float mx = kNegInf;
-  for (int x = x0; x < x0 + ns; ++x) mx = fmaxf(mx, c.part_lse[(int64_t)x * hl + rem]);
   const float le = c.extra_lse ? c.extra_lse[row] : kNegInf;
-  mx = fmaxf(mx, le);
+  // split LSEs, 64 at a time across the lanes: max first
+  float mx = le;
+  for (int x = lane; x < ns; x += 64) mx = fmaxf(mx, c.part_lse[(int64_t)(x0 + x) * hl + rem]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
   if (mx != kNegInf) {
-    for (int x = x0; x < x0 + ns; ++x) {
-      const int64_t pr = (int64_t)x * hl + rem;
-      const float w = expf(c.part_lse[pr] - mx);
-      wsum += w;
-      const float* po = c.part_o + pr * D + lane * PER;
+    for (int x1 = 0; x1 < ns; x1 += 64) {
+      const int nx = min(64, ns - x1);
+      // lane j holds the weight of split x1 + j
+      const float wl = lane < nx ? expf(c.part_lse[(int64_t)(x0 + x1 + lane) * hl + rem] - mx) : 0.f;
+      int j = 0;
+      for (; j + 4 <= nx; j += 4) {   // four partial rows in flight
+        float w4[4];
+        f32x4 v4[4];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, po[i], acc[i]);
+        for (int u = 0; u < 4; ++u) {
+          w4[u] = __shfl(wl, j + u, 64);
+          const float* po = c.part_o + ((int64_t)(x0 + x1 + j + u) * hl + rem) * D + lane * PER;
+          if constexpr (PER == 2) {
+            const f32x4 t = {po[0], po[1], 0.f, 0.f};
+            v4[u] = t;
+          } else {
+            const f32x4 t = {po[0], 0.f, 0.f, 0.f};
+            v4[u] = t;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wsum += w4[u];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w4[u], v4[u][i], acc[i]);
+        }
+      }
+      for (; j < nx; ++j) {
+        const float w = __shfl(wl, j, 64);
+        const float* po = c.part_o + ((int64_t)(x0 + x1 + j) * hl + rem) * D + lane * PER;
+        wsum += w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, po[i], acc[i]);
+      }
     }
     if (c.extra_lse) {
       const float w = expf(le - mx);
@@ -621,9 +834,10 @@ __global__ void __launch_bounds__(256) merge_kernel(int64_t rows, int D, const f
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int D, int QT, bool P>
+template <int D, int QT, int NW, int NS, bool PP, int WPC, bool P>
 static int launch_bf16(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16<D, QT, P>), dim3(a.grid), dim3(256), 0, s, a);
+  constexpr int minw = (NW * WPC + 3) / 4;   // waves per SIMD when WPC workgroups share a CU
+  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, PP, minw, P>), dim3(a.grid), dim3(64 * NW), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -633,24 +847,25 @@ static int launch_f32(const AttnArgs& a, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-int launch_attn(const AttnArgs& a, int dtype, int head_dim, int qt, bool partial, void* stream) {
+template <int D>
+static int launch_bf16_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
+  switch (cfg) {
+#define FB_CFG_LAUNCH(ID, QT, NW, NS, PP, WPC, PART) \
+    case ID: return launch_bf16<D, QT, NW, NS, PP, WPC, (PART) != 0>(a, s);
+    FB_BF16_CFGS(FB_CFG_LAUNCH)
+#undef FB_CFG_LAUNCH
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partial, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (a.grid == 0) return 0;
   if (dtype == 0) {  // fp32
     if (head_dim == 64) return partial ? launch_f32<64, true>(a, s) : launch_f32<64, false>(a, s);
     return partial ? launch_f32<128, true>(a, s) : launch_f32<128, false>(a, s);
   }
-#define FB_DISPATCH_QT(DD)                                                             \
-  switch (qt) {                                                                        \
-    case 1: return partial ? launch_bf16<DD, 1, true>(a, s) : launch_bf16<DD, 1, false>(a, s); \
-    case 2: return partial ? launch_bf16<DD, 2, true>(a, s) : launch_bf16<DD, 2, false>(a, s); \
-    default: return partial ? launch_bf16<DD, 4, true>(a, s) : launch_bf16<DD, 4, false>(a, s); \
-  }
-  if (head_dim == 64) {
-    FB_DISPATCH_QT(64)
-  }
-  FB_DISPATCH_QT(128)
-#undef FB_DISPATCH_QT
+  return head_dim == 64 ? launch_bf16_cfg<64>(a, cfg, s) : launch_bf16_cfg<128>(a, cfg, s);
 }
 
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream) {

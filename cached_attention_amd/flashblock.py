@@ -23,7 +23,8 @@ FB_F32, FB_BF16 = 0, 1
 FB_MODE_CACHED, FB_MODE_FULL = 0, 1
 FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 
-EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_merge", "fb_step",
+EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
+           "fb_block_attn", "fb_merge", "fb_step",
            "fb_status_string", "fb_last_error", "fb_abi_version")
 
 
@@ -76,6 +77,10 @@ def lib() -> ctypes.CDLL:
         l.fb_workspace_size.restype = sz
         l.fb_prefix_attn.argtypes = [D, P, P, P, S, P, P, P, sz, P]
         l.fb_prefix_attn.restype = i32
+        l.fb_prefix_partials.argtypes = [D, P, P, P, S, P, sz, P]
+        l.fb_prefix_partials.restype = i32
+        l.fb_prefix_combine.argtypes = [D, S, P, P, P, P, P, sz, P]
+        l.fb_prefix_combine.restype = i32
         l.fb_block_attn.argtypes = [D, P, P, P, P, P, P, P, P]
         l.fb_block_attn.restype = i32
         l.fb_merge.argtypes = [i64, i32, P, P, P, P, P, P, P]
@@ -171,6 +176,18 @@ def fb_prefix_attn(desc: Desc, q_blk, k_pre, v_pre, sparse: Optional[Sparse], o_
                    ws_bytes: int, stream=None) -> None:
     _check(lib().fb_prefix_attn(desc.ref, _ptr(q_blk), _ptr(k_pre), _ptr(v_pre), _sref(sparse), _ptr(o_ext),
                                 _ptr(lse_ext), _ptr(ws), ws_bytes, _stream(stream)), "fb_prefix_attn")
+
+
+def fb_prefix_partials(desc: Desc, q_blk, k_pre, v_pre, sparse: Optional[Sparse], ws, ws_bytes: int,
+                       stream=None) -> None:
+    _check(lib().fb_prefix_partials(desc.ref, _ptr(q_blk), _ptr(k_pre), _ptr(v_pre), _sref(sparse), _ptr(ws),
+                                    ws_bytes, _stream(stream)), "fb_prefix_partials")
+
+
+def fb_prefix_combine(desc: Desc, sparse: Optional[Sparse], extra_o, extra_lse, o_ext, lse_ext, ws,
+                      ws_bytes: int, stream=None) -> None:
+    _check(lib().fb_prefix_combine(desc.ref, _sref(sparse), _ptr(extra_o), _ptr(extra_lse), _ptr(o_ext),
+                                   _ptr(lse_ext), _ptr(ws), ws_bytes, _stream(stream)), "fb_prefix_combine")
 
 
 def fb_block_attn(desc: Desc, q_blk, k_blk, v_blk, o_ext, lse_ext, o, lse_out=None, stream=None) -> None:

@@ -121,6 +121,22 @@ fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre,
                          const void* v_pre, const fb_sparse* sp, float* o_ext,
                          float* lse_ext, void* ws, size_t ws_bytes, void* stream);
 
+/* The two steps fb_prefix_attn is made of, callable on their own.
+ * fb_prefix_partials: the split-KV pass only -- one normalised partial and its
+ * natural-log LSE per (split, query head, block position), written to `ws` in
+ * the layout fb_prefix_combine reads for the same (d, sp).
+ * fb_prefix_combine: log-sum-exp combination of those partials (the merge
+ * equation applied across the splits), optionally folding in one more partial
+ * (extra_o [B][Hq][Lb][D], extra_lse [B][Hq][Lb], both or neither -- the
+ * sparse variant's cached residual), into o_ext / lse_ext.  `sp` must be the
+ * same fb_sparse (or NULL) as for the partials call. */
+fb_status fb_prefix_partials(const fb_desc* d, const void* q_blk, const void* k_pre,
+                             const void* v_pre, const fb_sparse* sp, void* ws,
+                             size_t ws_bytes, void* stream);
+fb_status fb_prefix_combine(const fb_desc* d, const fb_sparse* sp, const float* extra_o,
+                            const float* extra_lse, float* o_ext, float* lse_ext,
+                            const void* ws, size_t ws_bytes, void* stream);
+
 /* Block-internal attention (Core Mechanism: A_in over J_in, bidirectional)
  * of every block query over the block's own keys, merged with (o_ext, lse_ext)
  * by the merge equation when those are non-NULL (both or neither), written to
