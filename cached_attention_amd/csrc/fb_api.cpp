@@ -48,11 +48,10 @@ int prefix_cfg(const fb_desc* d) {
   return rows <= 32 ? FB_PREFIX_CFG_32 : rows <= 64 ? FB_PREFIX_CFG_64 : rows <= 128 ? FB_PREFIX_CFG_128
                                                                                      : FB_PREFIX_CFG_256;
 #else
-  // measured on MI355X: two independent workgroups per CU for up to 128 rows
+  // measured on MI355X: two independent workgroups per CU, each 2-stage
   // (their waves drift apart, so one's softmax overlaps the other's MFMAs);
-  // the eight-wave ping-pong workgroup for 256 rows
-  return rows <= 32 ? fb::CFG_P32_X2 : rows <= 64 ? fb::CFG_P64_X2 : rows <= 128 ? fb::CFG_P128_X2
-                                                                                 : fb::CFG_P256_PP;
+  // 256-row KV heads take two 128-row tiles that share K/V through L2
+  return rows <= 32 ? fb::CFG_P32_X2 : rows <= 64 ? fb::CFG_P64_X2 : fb::CFG_P128_X2;
 #endif
 }
 int block_cfg(const fb_desc* d) {

@@ -254,57 +254,27 @@ __device__ __forceinline__ int kv_swz(int key) {
   return D == 128 ? ((key & 7) << 1) : ((key & 3) << 1);
 }
 
-// LDS reads of the MFMA operands are written as asm blocks that end with
-// their own lgkmcnt wait, so no read is left in flight when a block returns.
-// The compiler cannot tell these reads apart from direct-to-LDS writes still
-// in flight to other stages and would otherwise drain every outstanding load
-// before each of them.
-
-// four 16-byte reads (K fragments) at a + 0, STRIDE, 2*STRIDE, 3*STRIDE
-template <int STRIDE>
-__device__ __forceinline__ void lds_read4_rows(uint32_t a, u32x4 out[4]) {
+// One direct-to-LDS load: 64 lanes x 16 bytes from sbase + voff[lane] into
+// LDS at lds (M0), one contiguous 1 KB block.  Written as asm so that the
+// compiler, which cannot tell these asynchronous LDS writes apart from the
+// operand reads of other stages, does not drain every load in flight before
+// each LDS read; completion is tracked explicitly with per-stage vmcnt waits.
+// The instruction has no register outputs.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* sbase) {
+  // both operands are wave-uniform by construction; readfirstlane makes that
+  // explicit so they live in SGPRs
+  // (readfirstlane returns a signed int: widen through uint32_t, never by
+  // sign extension, or a low word with bit 31 set corrupts the high word)
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(lds);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:%5\n\t"
-      "ds_read_b128 %2, %4 offset:%6\n\t"
-      "ds_read_b128 %3, %4 offset:%7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
-      : "v"(a), "i"(STRIDE), "i"(2 * STRIDE), "i"(3 * STRIDE)
-      : "memory");
-}
-
-// four 16-byte reads at a0..a3 + OFF
-template <int OFF>
-__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4 out[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4 offset:%8\n\t"
-      "ds_read_b128 %1, %5 offset:%8\n\t"
-      "ds_read_b128 %2, %6 offset:%8\n\t"
-      "ds_read_b128 %3, %7 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF)
-      : "memory");
-}
-
-// four pairs of transpose reads (V^T fragment halves at +OFF and +OFF+HALF)
-template <int OFF, int HALF>
-__device__ __forceinline__ void lds_tr_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x2 lo[4],
-                                             u32x2 hi[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
-        "=&v"(hi[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(OFF), "i"(OFF + HALF)
+      "s_mov_b32 m0, %0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(l), "v"(voff), "s"(bs)
       : "memory");
 }
 
@@ -333,6 +303,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  // waves w and w + NW/2 share a SIMD: the upper half lags
   const bool lagging = PP && wave >= NW / 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
@@ -391,14 +362,13 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < IPW; ++u) {
       const int jj = jj0 + u;
-      uint32_t off = lane_part[u & 1] + (uint32_t)((jj - (u & 1)) * RPI * row_bytes);
       if (nvalid < kTile) {   // ragged tile: rows past the end re-read the last key (masked later)
         const int row = jj * RPI + lane / CH;
         const int srow = row < nvalid ? row : nvalid - 1;
-        off = (uint32_t)(srow * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16;
+        dma16(dst + u * 1024, (uint32_t)(srow * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16, g);
+      } else {
+        dma16(dst + u * 1024, lane_part[u & 1] + (uint32_t)((jj - (u & 1)) * RPI * row_bytes), g);
       }
-      __builtin_amdgcn_global_load_lds((const void*)(g + off), (FB_LDS void*)(uintptr_t)(dst + u * 1024), 16, 0,
-                                       0);
     }
   };
 
@@ -417,21 +387,24 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // S^T = K Q^T for the tile at LDS offset kb; k-step outer so that the
   // 4 x QT accumulators of a step are independent MFMA chains
   auto scores = [&](uint32_t kb) {
+    if constexpr (PP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 kraw[4];   // keys 16*tt + l16, tt = 0..3, 16-byte slot 4*ks + lg
-      lds_read4_rows<16 * 2 * D>(kb + koff[ks], kraw);
+      const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
+      bf16x8 kf[4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) kf[tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw[tt]), qf[qt][ks],
-                                                              s[tt][qt], 0, 0, 0);
+          s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt], qf[qt][ks], s[tt][qt], 0, 0, 0);
     }
+    if constexpr (PP) __builtin_amdgcn_s_setprio(0);
   };
 
   // exact row maxima of the tile (4 lane groups share a query column)
@@ -513,26 +486,22 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l_run[qt] += rs[qt];
-    auto pv_half = [&](auto JJ) {
-      constexpr int jj = decltype(JJ)::value;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    if constexpr (PP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int d0 = 0; d0 < DT; d0 += 4) {
-        u32x2 lo[4], hi[4];
-        lds_tr_read4<jj * 32 * 2 * D, 16 * 2 * D>(vb + vlane + 32 * ((d0 + 0) ^ vkx), vb + vlane + 32 * ((d0 + 1) ^ vkx),
-                                                vb + vlane + 32 * ((d0 + 2) ^ vkx), vb + vlane + 32 * ((d0 + 3) ^ vkx),
-                                                lo, hi);
+    for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x4 w = {lo[u][0], lo[u][1], hi[u][0], hi[u][1]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t va = vb + vlane + 32 * (dt ^ vkx) + jj * 32 * 2 * D;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)va);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)(va + 16 * 2 * D));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
-            oacc[d0 + u][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jj][qt], oacc[d0 + u][qt], 0, 0, 0);
-        }
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jj][qt], oacc[dt][qt], 0, 0, 0);
       }
-    };
-    pv_half(IC<0>{});
-    pv_half(IC<1>{});
+    }
+    if constexpr (PP) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- pipeline: position j of the queue = tile k + j; stage of tile k = st ----
@@ -570,9 +539,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     } else {
       if (cur && lagging) sync_issue();
       if (wave_active && prev_ok) softmax_pv(prev_vb, prev_nv);
+      __builtin_amdgcn_sched_barrier(0);   // phases stay apart: bounds live registers
       if (!cur) break;          // that was the last tile's softmax
       if (!lagging) sync_issue();
       if (wave_active) scores(kb);
+      __builtin_amdgcn_sched_barrier(0);
       prev_ok = true;
       prev_nv = q_nv[0];
       prev_vb = kb + TBYTES;
