@@ -104,6 +104,9 @@ def main() -> int:
     ap.add_argument("--r", type=int, default=8)
     ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
                     help="prefix KV cache layout: head-major [Hkv][T][D] or token-major [T][Hkv][D]")
+    ap.add_argument("--sparse", action="store_true",
+                    help="chunk-sparse variant: cached residual of the unselected 64-token chunks plus a fresh "
+                         "partial over the selected ones (workloads with a sparse keep fraction)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale FETCH_SIZE / WRITE_SIZE "
@@ -172,8 +175,15 @@ def main() -> int:
         k0, v0 = dev_kv(kp), dev_kv(vp)
         layers.append([(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(N_LAYERS - 1)])
     steps_dev = [[(dev(b.q[s]), dev(b.k[s]), dev(b.v[s])) for s in range(w.steps)] for b in blocks]
+    chunks = None
+    if args.sparse:
+        if w.sparse_keep <= 0:
+            print(f"workload {w.name} has no sparse variant", file=sys.stderr)
+            return 2
+        lens0 = [int(prefix.offsets[b + 1] - prefix.offsets[b]) for b in range(w.batch)]
+        chunks = torch.from_numpy(wl.make_chunk_selection(w, lens0))
     states = [AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, block_prefix[j][2],
-                            pre_strides=pre_strides[j])
+                            pre_strides=pre_strides[j], chunks=chunks)
               for j in range(len(blocks))]
     torch.cuda.synchronize()
 
@@ -227,15 +237,19 @@ def main() -> int:
     n_k = max(20, args.steps)
     rot = [0]
 
+    sel = None
+    if args.sparse:   # the prefix work of every step: the selected chunks
+        sel = fbl.Sparse(st0.chunks, int(st0.chunks.shape[-1]), 64, fbl.FB_CHUNKS_SELECTED)
+
     def prefix_kernel():
         kp, vp = layers[0][rot[0] % N_LAYERS]
         rot[0] += 1
-        fbl.fb_prefix_partials(st0.desc, q0, kp, vp, None, st0.ws, st0.ws_bytes)
+        fbl.fb_prefix_partials(st0.desc, q0, kp, vp, sel, st0.ws, st0.ws_bytes)
 
     for _ in range(3):
         prefix_kernel()
     ms_prefix_kernel = timed(prefix_kernel, n_k)
-    ms_combine = timed(lambda: fbl.fb_prefix_combine(st0.desc, None, None, None, st0.o_ext, st0.lse_ext,
+    ms_combine = timed(lambda: fbl.fb_prefix_combine(st0.desc, sel, None, None, st0.o_ext, st0.lse_ext,
                                                      st0.ws, st0.ws_bytes), n_k)
     qb, kb, vb = steps_dev[0][1]
     ms_block = timed(lambda: fbl.fb_block_attn(st0.desc, qb, kb, vb, st0.o_ext, st0.lse_ext, st0.o), n_k)
@@ -258,7 +272,11 @@ def main() -> int:
 
     lens = block_prefix[0][2]
     lens = [int(lens[b + 1] - lens[b]) for b in range(w.batch)]
-    pb, pf, bb, bf = algorithmic(w, lens)
+    sparse_tokens = None
+    if args.sparse:
+        k_sel = int(st0.chunks.shape[-1])
+        sparse_tokens = sum(min(64 * k_sel, l) for l in lens)   # selected keys per KV head, all streams
+    pb, pf, bb, bf = algorithmic(w, lens, sparse_tokens)
     prefix_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
     prefix_tflops = pf / (ms_prefix_kernel * 1e-3) / 1e12
 
@@ -280,6 +298,8 @@ def main() -> int:
             "block_len": w.block_len, "prefix_len": lens if w.batch > 1 else lens[0],
             "denoise_steps": w.steps, "blocks": len(blocks), "refresh_period": r,
             "kv_layout": "head-major [Hkv][T][D]" if head_major else "token-major [T][Hkv][D]",
+            "sparse": (f"{int(st0.chunks.shape[-1])} of 64-token chunks per KV head selected; residual cached"
+                       if args.sparse else None),
             "step": "one block of denoise_steps attention steps, one layer",
         },
         "full_recompute": {"value": q_tokens / (ms_full * 1e-3), "unit": "query-tok/s", "ms_per_step": ms_full},
@@ -293,7 +313,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": prefix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": prefix_gbs / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials)",
+            "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials" + (", selected chunks)" if args.sparse else ")"),
             "algorithmic_bytes_per_launch": pb,
             "mfma_tflops": prefix_tflops, "mfma_frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS,
         },
