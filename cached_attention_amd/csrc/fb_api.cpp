@@ -56,7 +56,11 @@ int prefix_cfg(const fb_desc* d) {
 }
 int block_cfg(const fb_desc* d) {
   const int rows = (d->hq / d->hkv) * d->block_len;
+#ifdef FB_BLOCK_CFG_BIG
+  return rows >= 1024 ? FB_BLOCK_CFG_BIG : fb::CFG_B64;
+#else
   return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B64;
+#endif
 }
 // fp32 inputs run the VALU kernel: 64 rows per workgroup, 2 per CU.
 fb::CfgInfo pass_info(const fb_desc* d, int cfg) {

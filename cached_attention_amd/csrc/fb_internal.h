@@ -10,23 +10,23 @@ enum ChunkMode : int32_t { CHUNKS_ALL = 0, CHUNKS_SELECTED = 1, CHUNKS_COMPLEMEN
 constexpr int kTile = 64;  // keys per LDS tile
 
 // bf16 kernel configurations.  X(id, rows per wave / 16, waves, LDS stages,
-// ping-pong schedule, resident workgroups per CU, pass: 1 = split partial of
-// the prefix pass, 0 = block pass with merge).  Query rows per workgroup =
-// waves * 16 * (rows per wave / 16).
-#define FB_BF16_CFGS(X)                                                       \
-  X(0, 1, 2, 4, false, 1, 1)   /* prefix  32 rows: 2 waves x 16          */ \
-  X(1, 1, 4, 4, false, 1, 1)   /* prefix  64 rows: 4 waves x 16          */ \
-  X(2, 2, 4, 4, false, 1, 1)   /* prefix 128 rows: 4 waves x 32          */ \
-  X(3, 2, 8, 4, false, 1, 1)   /* prefix 256 rows: 8 waves x 32          */ \
-  X(4, 1, 4, 2, false, 2, 0)   /* block   64 rows                        */ \
-  X(5, 1, 8, 2, false, 1, 0)   /* block  128 rows                        */ \
-  X(6, 2, 8, 4, true, 1, 1)    /* prefix 256 rows, ping-pong             */ \
-  X(7, 2, 4, 2, false, 2, 1)   /* prefix 128 rows, 2 workgroups per CU   */ \
-  X(8, 4, 4, 4, false, 1, 1)   /* prefix 256 rows: 4 waves x 64          */ \
-  X(9, 1, 2, 2, false, 2, 1)   /* prefix  32 rows, 2 workgroups per CU   */ \
-  X(10, 1, 4, 2, false, 2, 1)  /* prefix  64 rows, 2 workgroups per CU   */ \
-  X(11, 1, 8, 4, true, 1, 1)   /* prefix 128 rows: 8 waves x 16, ping-pong */ \
-  X(12, 1, 8, 4, false, 1, 1)  /* prefix 128 rows: 8 waves x 16          */
+// resident workgroups per CU, pass: 1 = split partial of the prefix pass,
+// 0 = block pass with merge).  Query rows per workgroup = waves * 16 *
+// (rows per wave / 16).
+#define FB_BF16_CFGS(X)                                                \
+  X(0, 1, 2, 4, 1, 1)    /* prefix  32 rows: 2 waves x 16            */ \
+  X(1, 1, 4, 4, 1, 1)    /* prefix  64 rows: 4 waves x 16            */ \
+  X(2, 2, 4, 4, 1, 1)    /* prefix 128 rows: 4 waves x 32            */ \
+  X(3, 2, 8, 4, 1, 1)    /* prefix 256 rows: 8 waves x 32            */ \
+  X(4, 1, 4, 2, 2, 0)    /* block   64 rows                          */ \
+  X(5, 1, 8, 2, 1, 0)    /* block  128 rows                          */ \
+  X(7, 2, 4, 2, 2, 1)    /* prefix 128 rows, 2 workgroups per CU     */ \
+  X(8, 4, 4, 4, 1, 1)    /* prefix 256 rows: 4 waves x 64            */ \
+  X(9, 1, 2, 2, 2, 1)    /* prefix  32 rows, 2 workgroups per CU     */ \
+  X(10, 1, 4, 2, 2, 1)   /* prefix  64 rows, 2 workgroups per CU     */ \
+  X(12, 1, 8, 4, 1, 1)   /* prefix 128 rows: 8 waves x 16            */ \
+  X(18, 2, 8, 2, 1, 0)   /* block  256 rows: 8 waves x 32            */ \
+  X(19, 2, 4, 2, 2, 0)   /* block  128 rows, 2 workgroups per CU     */
 
 enum KernelCfg : int32_t {
   CFG_P32 = 0,
@@ -35,13 +35,13 @@ enum KernelCfg : int32_t {
   CFG_P256 = 3,
   CFG_B64 = 4,
   CFG_B128 = 5,
-  CFG_P256_PP = 6,
   CFG_P128_X2 = 7,
   CFG_P256_Q4 = 8,
   CFG_P32_X2 = 9,
   CFG_P64_X2 = 10,
-  CFG_P128_W8PP = 11,
   CFG_P128_W8 = 12,
+  CFG_B256 = 18,
+  CFG_B128_X2 = 19,
 };
 
 struct CfgInfo {
@@ -50,7 +50,7 @@ struct CfgInfo {
 };
 inline CfgInfo cfg_info(int cfg) {
   switch (cfg) {
-#define FB_CFG_INFO(ID, QT, NW, NS, PP, WPC, PART) \
+#define FB_CFG_INFO(ID, QT, NW, NS, WPC, PART) \
     case ID: return {(NW) * 16 * (QT), WPC};
     FB_BF16_CFGS(FB_CFG_INFO)
 #undef FB_CFG_INFO

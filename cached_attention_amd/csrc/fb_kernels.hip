@@ -204,19 +204,17 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 // ring, DIST tiles ahead of the tile being computed; each wave waits only for
 // the tile it is about to read (per-stage vmcnt), then one barrier per tile.
 //
-// Eight-wave workgroups run a ping-pong schedule: waves 4..7 lag waves 0..3
-// by half a tile (they run the softmax and PV product of tile k-1 while the
-// leading waves compute the scores of tile k), so the two waves sharing a
-// SIMD are in different phases and one's VALU work overlaps the other's MFMA
-// work.  The lag keeps one extra stage in use, so these workgroups prefetch
-// NS-2 tiles ahead instead of NS-1.
+// LDS operands are read ahead into registers: the K fragments of k-step
+// ks+1 while the MFMAs of step ks run, and the V^T fragments kVAhead MFMA
+// groups ahead of their use (the first ones before the softmax, whose VALU
+// work covers their latency).
 //
-// Running max: the first tile of a pass sets it from the exact row maxima;
-// later tiles compute p = exp2(s*c - m) against it directly and only fall back
-// to exact maxima plus a rescale of O and l when some row's partial sum shows
-// p beyond 2^64 (or not finite).  Every p stays far inside the fp32 / bf16
-// range and the normalised result is unchanged, while the common tile skips
-// the max reduction altogether.
+// Running max: the first tile of a pass (peeled out of the tile loop) sets it
+// from the exact row maxima; later tiles compute p = exp2(s*c - m) against it
+// directly and only fall back to exact maxima plus a rescale of O and l when
+// some row's partial sum shows p beyond 2^64 (or not finite).  Every p stays
+// far inside the fp32 / bf16 range and the normalised result is unchanged,
+// while the common tile skips the max reduction altogether.
 
 constexpr float kOverflowSum = 1.8446744e19f;  // 2^64: partial row sums beyond it take the exact-max path
 
@@ -278,7 +276,12 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* s
       : "memory");
 }
 
-template <int D, int QT, int NW, int NS, bool PP, int MINW, bool PARTIAL>
+#ifndef FB_V_AHEAD
+#define FB_V_AHEAD 2
+#endif
+constexpr int kVAhead = FB_V_AHEAD;   // V^T fragment groups read ahead of their MFMAs
+
+template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL>
 __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the score MFMA
   constexpr int DT = D / 16;                  // 16-row d tiles of O^T
@@ -289,9 +292,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int IPT = TBYTES / 1024;          // 1 KB direct-to-LDS loads per tile and tensor
   constexpr int IPW = 2 * IPT / NW;           // loads per wave per tile
   constexpr int RPI = 1024 / (2 * D);         // key rows per load instruction
-  constexpr int DIST = PP ? NS - 2 : NS - 1;  // prefetch distance in tiles
+  constexpr int DIST = NS - 1;                // prefetch distance in tiles
+  constexpr int NG = 2 * DT;                  // MFMA groups of the PV product
   static_assert(IPT % IPW == 0 && IPW % 2 == 0, "each wave loads an even run of one tensor");
-  static_assert(NS >= 2 && NS <= 4 && DIST >= 1, "2..4 stages");
+  static_assert(NS >= 2 && NS <= 4, "2..4 stages");
   static_assert((DIST - 1) * IPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
@@ -300,11 +304,9 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: DMA operands stay scalar
   const int l16 = lane & 15;
   const int lg = lane >> 4;
-  // waves w and w + NW/2 share a SIMD: the upper half lags
-  const bool lagging = PP && wave >= NW / 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
   // ---- query fragments (B operand of the score MFMA) ----
@@ -385,47 +387,56 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   f32x4 s[4][QT];
 
   // S^T = K Q^T for the tile at LDS offset kb; k-step outer so that the
-  // 4 x QT accumulators of a step are independent MFMA chains
+  // 4 x QT accumulators of a step are independent MFMA chains.  The K
+  // fragments of step ks+1 are read while the MFMAs of step ks run; the
+  // scheduling fences keep the compiler from sinking the reads next to
+  // their MFMAs, where each group would wait out the LDS latency.
   auto scores = [&](uint32_t kb) {
-    if constexpr (PP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[KS][4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
+    auto kload = [&](int ks) {
+      const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
+    };
+    kload(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
-      bf16x8 kf[4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) kf[tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
+      if (ks + 1 < KS) kload(ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt], qf[qt][ks], s[tt][qt], 0, 0, 0);
+          s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], qf[qt][ks], s[tt][qt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (PP) __builtin_amdgcn_s_setprio(0);
   };
 
   // exact row maxima of the tile (4 lane groups share a query column)
+  auto row_max = [&](int qt) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt][i]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    return mx * c;
+  };
+  // raise the running max to the tile's exact maxima, rescaling O and l
   auto raise_max = [&]() {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float mx = kNegInf;
+      const float m_new = fmaxf(m_run[qt], row_max(qt));
+      const float alpha = m_new == m_run[qt] ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);   // 0 when m_run = -inf
+      m_run[qt] = m_new;
+      l_run[qt] *= alpha;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt][i]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run[qt], mx * c);
-      if (m_new != m_run[qt]) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);   // 0 when m_run = -inf
-        m_run[qt] = m_new;
-        l_run[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-      }
+      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
     }
   };
 
@@ -463,8 +474,24 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   };
 
   // softmax of the scores in s (tile with nvalid keys), then O^T += V^T P^T
-  // with V at LDS offset vb
-  auto softmax_pv = [&](uint32_t vb, int nvalid) {
+  // with V at LDS offset vb.  The PV product runs in NG groups (key half jj,
+  // d tile dt), each one V^T fragment (two transpose reads) and QT MFMAs.
+  // FIRST: the pass's first tile, where O and l are still zero, so the exact
+  // maxima are set without a rescale.
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  auto softmax_pv = [&](uint32_t vb, int nvalid, auto first_tag) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    bf16x8 vf[NG];
+    auto vload = [&](int g) {
+      const int jj = g / DT, dt = g % DT;
+      const uint32_t va = vb + vlane + 32 * (dt ^ vkx) + jj * 32 * 2 * D;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)va);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)(va + 16 * 2 * D));
+      vf[g] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+#pragma unroll
+    for (int g = 0; g < kVAhead; ++g) vload(g);
+    __builtin_amdgcn_sched_barrier(0);
     if (nvalid < kTile) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -476,32 +503,25 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
             if (dead) s[tt][qt][i] = kNegInf;
         }
     }
-    bool first = false;
+    if constexpr (FIRST) {
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) first |= m_run[qt] == kNegInf;
-    if (__any(first)) raise_max();
+      for (int qt = 0; qt < QT; ++qt) m_run[qt] = fmaxf(m_run[qt], row_max(qt));
+    }
     if (!__all(exps())) {   // rare: a row's scores jumped far above the running max
       raise_max();
       exps();
     }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l_run[qt] += rs[qt];
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    if constexpr (PP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
+    for (int g = 0; g < NG; ++g) {
+      if (g + kVAhead < NG) vload(g + kVAhead);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint32_t va = vb + vlane + 32 * (dt ^ vkx) + jj * 32 * 2 * D;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)va);
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)(va + 16 * 2 * D));
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-          oacc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[jj][qt], oacc[dt][qt], 0, 0, 0);
-      }
+      for (int qt = 0; qt < QT; ++qt)
+        oacc[g % DT][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g], pf[g / DT][qt], oacc[g % DT][qt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (PP) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- pipeline: position j of the queue = tile k + j; stage of tile k = st ----
@@ -514,39 +534,21 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
   }
   int st = 0;
-  bool prev_ok = false;      // ping-pong lagging waves: scores of the previous tile wait in s
-  int prev_nv = 0;
-  uint32_t prev_vb = 0;
-  for (;;) {
-    const bool cur = q_have[0];
-    if (!cur && !(PP && lagging && prev_ok)) break;
-    auto sync_issue = [&]() {
-      int after = 0;
+  // one tile: wait for it (tiles issued after it may stay in flight), one
+  // barrier (every wave is done with the stage refilled next), issue the tile
+  // DIST ahead, compute, advance the queue
+  auto tile_step = [&](auto first_tag) {
+    int after = 0;
 #pragma unroll
-      for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
-      wait_vmcnt_tiles<IPW>(after);
-      lds_dma_barrier();
-      q_have[DIST] = q_have[DIST - 1] && next_tile(wk.it, q_tok[DIST], q_nv[DIST]);
-      if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
-    };
+    for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
+    wait_vmcnt_tiles<IPW>(after);
+    lds_dma_barrier();
+    q_have[DIST] = q_have[DIST - 1] && next_tile(wk.it, q_tok[DIST], q_nv[DIST]);
+    if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
     const uint32_t kb = lds0 + st * STAGE;
-    if constexpr (!PP) {
-      sync_issue();
-      if (wave_active) {
-        scores(kb);
-        softmax_pv(kb + TBYTES, q_nv[0]);
-      }
-    } else {
-      if (cur && lagging) sync_issue();
-      if (wave_active && prev_ok) softmax_pv(prev_vb, prev_nv);
-      __builtin_amdgcn_sched_barrier(0);   // phases stay apart: bounds live registers
-      if (!cur) break;          // that was the last tile's softmax
-      if (!lagging) sync_issue();
-      if (wave_active) scores(kb);
-      __builtin_amdgcn_sched_barrier(0);
-      prev_ok = true;
-      prev_nv = q_nv[0];
-      prev_vb = kb + TBYTES;
+    if (wave_active) {
+      scores(kb);
+      softmax_pv(kb + TBYTES, q_nv[0], first_tag);
     }
 #pragma unroll
     for (int j = 0; j < DIST; ++j) {
@@ -556,9 +558,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
     q_have[DIST] = false;
     st = st + 1 == NS ? 0 : st + 1;
-  }
-  if constexpr (PP) {
-    if (!lagging && wave_active && prev_ok) softmax_pv(prev_vb, prev_nv);
+  };
+  if (q_have[0]) {
+    tile_step(IC<1>{});
+    while (q_have[0]) tile_step(IC<0>{});
   }
 
   if (!wave_active) return;
@@ -805,10 +808,10 @@ __global__ void __launch_bounds__(256) merge_kernel(int64_t rows, int D, const f
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int D, int QT, int NW, int NS, bool PP, int WPC, bool P>
+template <int D, int QT, int NW, int NS, int WPC, bool P>
 static int launch_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int minw = (NW * WPC + 3) / 4;   // waves per SIMD when WPC workgroups share a CU
-  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, PP, minw, P>), dim3(a.grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, minw, P>), dim3(a.grid), dim3(64 * NW), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -821,8 +824,8 @@ static int launch_f32(const AttnArgs& a, hipStream_t s) {
 template <int D>
 static int launch_bf16_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
   switch (cfg) {
-#define FB_CFG_LAUNCH(ID, QT, NW, NS, PP, WPC, PART) \
-    case ID: return launch_bf16<D, QT, NW, NS, PP, WPC, (PART) != 0>(a, s);
+#define FB_CFG_LAUNCH(ID, QT, NW, NS, WPC, PART) \
+    case ID: return launch_bf16<D, QT, NW, NS, WPC, (PART) != 0>(a, s);
     FB_BF16_CFGS(FB_CFG_LAUNCH)
 #undef FB_CFG_LAUNCH
     default: return (int)hipErrorInvalidValue;
