@@ -209,14 +209,18 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 // groups ahead of their use (the first ones before the softmax, whose VALU
 // work covers their latency).
 //
-// Running max: the first tile of a pass (peeled out of the tile loop) sets it
-// from the exact row maxima; later tiles compute p = exp2(s*c - m) against it
-// directly and only fall back to exact maxima plus a rescale of O and l when
-// some row's partial sum shows p beyond 2^64 (or not finite).  Every p stays
-// far inside the fp32 / bf16 range and the normalised result is unchanged,
-// while the common tile skips the max reduction altogether.
+// Softmax reference: each pass (one split of the prefix, or the block) runs
+// against a fixed per-row reference m, the exact row maxima of its first tile
+// (peeled out of the tile loop); every later tile computes p = exp2(s*c - m)
+// with no max reduction and no rescale of O.  The loop only keeps a lane-local
+// running max of the raw scores; after the last tile the workgroup checks
+// whether any score went more than 2^64 above its row's reference (p must
+// stay far inside the fp32 / bf16 range).  If one did -- rare: it takes a
+// score jump of about 44 nats within one split -- the pass is run again with
+// the exact maxima of the whole split as the reference, which no score can
+// exceed.  The normalised result does not depend on the reference.
 
-constexpr float kOverflowSum = 1.8446744e19f;  // 2^64: partial row sums beyond it take the exact-max path
+constexpr float kRefMargin = 64.f;   // log2 headroom of scores above the reference
 
 #define FB_LDS __attribute__((address_space(3)))
 
@@ -334,12 +338,15 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) oacc[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run[QT], l_run[QT];
+  float m_run[QT], l_run[QT], mx_lane[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = kNegInf;
     l_run[qt] = 0.f;
+    mx_lane[qt] = kNegInf;
   }
+  __shared__ int wg_redo;   // set by any wave whose scores outran the reference
+  if (tid == 0) wg_redo = 0;
 
   // ---- direct-to-LDS tile loads ----
   // Waves 0..NW/2-1 load K, the others V; wave w's IPW instructions cover the
@@ -358,7 +365,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     const int row = par * RPI + lane / CH;
     lane_part[par] = (uint32_t)(row * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16;
   }
-  auto issue = [&](int stage, int64_t tok0, int nvalid) {
+  auto issue = [&](int stage, int64_t tok0, int nvalid) __attribute__((always_inline)) {
     const char* g = gsrc + tok0 * row_bytes;
     const uint32_t dst = lds_dst + stage * STAGE;
 #pragma unroll
@@ -391,13 +398,13 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // fragments of step ks+1 are read while the MFMAs of step ks run; the
   // scheduling fences keep the compiler from sinking the reads next to
   // their MFMAs, where each group would wait out the LDS latency.
-  auto scores = [&](uint32_t kb) {
+  auto scores = [&](uint32_t kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     bf16x8 kf[KS][4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
-    auto kload = [&](int ks) {
+    auto kload = [&](int ks) __attribute__((always_inline)) {
       const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
@@ -417,7 +424,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   };
 
   // exact row maxima of the tile (4 lane groups share a query column)
-  auto row_max = [&](int qt) {
+  auto row_max = [&](int qt) __attribute__((always_inline)) {
     float mx = kNegInf;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -427,25 +434,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
     return mx * c;
   };
-  // raise the running max to the tile's exact maxima, rescaling O and l
-  auto raise_max = [&]() {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float m_new = fmaxf(m_run[qt], row_max(qt));
-      const float alpha = m_new == m_run[qt] ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);   // 0 when m_run = -inf
-      m_run[qt] = m_new;
-      l_run[qt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] *= alpha;
-    }
-  };
-
-  // p = exp2(s*c - m), packed to bf16 for the PV product; false if some
-  // partial row sum leaves the safe range
+  // p = exp2(s*c - m) against the reference, packed to bf16 for the PV
+  // product; row sums (this lane's 16 keys) in rs
   bf16x8 pf[2][QT];
   float rs[QT];
-  auto exps = [&]() -> bool {
-    bool ok = true;
+  auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float msub = m_run[qt] == kNegInf ? 0.f : m_run[qt];
@@ -463,26 +456,24 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
         pk[tt][1] = pack_bf16x2(p[2], p[3]);
       }
       rs[qt] = sum;
-      ok &= sum <= kOverflowSum || sum != sum;   // NaN inputs propagate, no retry
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         u32x4 pv = {pk[2 * jj][0], pk[2 * jj][1], pk[2 * jj + 1][0], pk[2 * jj + 1][1]};
         pf[jj][qt] = __builtin_bit_cast(bf16x8, pv);
       }
     }
-    return ok;
   };
 
   // softmax of the scores in s (tile with nvalid keys), then O^T += V^T P^T
   // with V at LDS offset vb.  The PV product runs in NG groups (key half jj,
   // d tile dt), each one V^T fragment (two transpose reads) and QT MFMAs.
-  // FIRST: the pass's first tile, where O and l are still zero, so the exact
-  // maxima are set without a rescale.
+  // FIRST: the pass's first tile, which sets the reference; later tiles feed
+  // the lane-local running max mx_lane instead.
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  auto softmax_pv = [&](uint32_t vb, int nvalid, auto first_tag) {
+  auto softmax_pv = [&](uint32_t vb, int nvalid, auto first_tag) __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_tag)::value;
     bf16x8 vf[NG];
-    auto vload = [&](int g) {
+    auto vload = [&](int g) __attribute__((always_inline)) {
       const int jj = g / DT, dt = g % DT;
       const uint32_t va = vb + vlane + 32 * (dt ^ vkx) + jj * 32 * 2 * D;
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)va);
@@ -505,12 +496,16 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
     if constexpr (FIRST) {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) m_run[qt] = fmaxf(m_run[qt], row_max(qt));
+      for (int qt = 0; qt < QT; ++qt) m_run[qt] = row_max(qt);
+    } else {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx_lane[qt] = fmaxf(mx_lane[qt], s[tt][qt][i]);
     }
-    if (!__all(exps())) {   // rare: a row's scores jumped far above the running max
-      raise_max();
-      exps();
-    }
+    exps();
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) l_run[qt] += rs[qt];
 #pragma unroll
@@ -528,16 +523,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   bool q_have[4] = {false, false, false, false};
   int64_t q_tok[4] = {0, 0, 0, 0};
   int q_nv[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < DIST; ++j) {
-    q_have[j] = (j == 0 || q_have[j - 1]) && next_tile(wk.it, q_tok[j], q_nv[j]);
-    if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
-  }
   int st = 0;
   // one tile: wait for it (tiles issued after it may stay in flight), one
   // barrier (every wave is done with the stage refilled next), issue the tile
   // DIST ahead, compute, advance the queue
-  auto tile_step = [&](auto first_tag) {
+  auto tile_step = [&](auto first_tag) __attribute__((always_inline)) {
     int after = 0;
 #pragma unroll
     for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
@@ -559,9 +549,44 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     q_have[DIST] = false;
     st = st + 1 == NS ? 0 : st + 1;
   };
-  if (q_have[0]) {
-    tile_step(IC<1>{});
+  // one pass over the tiles of the split; false if it has none
+  auto run_pass = [&](auto first_tag) __attribute__((always_inline)) -> bool {
+    st = 0;
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) {
+      q_have[j] = (j == 0 || q_have[j - 1]) && next_tile(wk.it, q_tok[j], q_nv[j]);
+      if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
+    }
+    if (!q_have[0]) return false;
+    tile_step(first_tag);
     while (q_have[0]) tile_step(IC<0>{});
+    return true;
+  };
+  const TileIter it0 = wk.it;
+  if (run_pass(IC<1>{})) {
+    // did a score outrun its row's reference by more than the margin?
+    bool redo = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = mx_lane[qt];
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx_lane[qt] = mx * c;   // exact row maxima over the split
+      redo |= wave_active && mx_lane[qt] > m_run[qt] + kRefMargin;
+    }
+    if (__any(redo) && lane == 0) wg_redo = 1;
+    __syncthreads();
+    if (wg_redo) {   // rare: again, against the split's exact maxima
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        m_run[qt] = fmaxf(m_run[qt], mx_lane[qt]);
+        l_run[qt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+      wk.it = it0;
+      run_pass(IC<0>{});
+    }
   }
 
   if (!wave_active) return;
