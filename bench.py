@@ -22,6 +22,7 @@ fp64 oracle timed on the host cores as a baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -40,6 +41,25 @@ N_LAYERS = 3
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the prefix kernel from profiles/hbm_traffic.md, or None.
+
+    The table records the sha256 of the kernel source the counters were taken
+    with; a row only counts while the source still hashes the same.
+    """
+    here = os.path.dirname(os.path.abspath(__file__))
+    table = os.path.join(here, "profiles", "hbm_traffic.md")
+    src = os.path.join(here, "cached_attention_amd", "csrc", "fb_kernels.hip")
+    if not (os.path.exists(table) and os.path.exists(src)):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(table):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] == workload and cells[1] == sha:
+            return float(cells[5])
+    return None
 
 
 def algorithmic(w, lens, sparse_tokens=None):
@@ -280,6 +300,26 @@ def main() -> int:
     prefix_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
     prefix_tflops = pf / (ms_prefix_kernel * 1e-3) / 1e12
 
+    # the dominant kernel's roofline: HBM below the ridge point, MFMA above it
+    mfma_bound = pf / pb > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": prefix_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": prefix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": prefix_gbs / HBM_PEAK_GBS}
+    traffic = measured_traffic(w.name) if not args.sparse and args.kv_layout == "head" else None
+    roof.update({
+        "traffic": traffic,
+        "traffic_source": ("profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, "
+                           "same kernel source)") if traffic is not None else None,
+        "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials" + (", selected chunks)" if args.sparse else ")"),
+        "algorithmic_bytes_per_launch": pb,
+        "algorithmic_flops_per_launch": pf,
+        "hbm_gbs": prefix_gbs, "hbm_frac": prefix_gbs / HBM_PEAK_GBS,
+        "mfma_tflops": prefix_tflops, "mfma_frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS,
+    })
+
     result = {
         "metric": METRIC,
         "value": q_tokens / (ms_cached * 1e-3),
@@ -310,13 +350,7 @@ def main() -> int:
                        "block_attn_merge": ms_block * 1e3},
         "drift_max_abs": max(drift),
         "drift_per_step": drift,
-        "roofline": {
-            "bound": "hbm", "achieved": prefix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": prefix_gbs / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials" + (", selected chunks)" if args.sparse else ")"),
-            "algorithmic_bytes_per_launch": pb,
-            "mfma_tflops": prefix_tflops, "mfma_frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS,
-        },
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")

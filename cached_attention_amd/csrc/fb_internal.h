@@ -26,7 +26,8 @@ constexpr int kTile = 64;  // keys per LDS tile
   X(10, 1, 4, 2, 2, 1)   /* prefix  64 rows, 2 workgroups per CU     */ \
   X(12, 1, 8, 4, 1, 1)   /* prefix 128 rows: 8 waves x 16            */ \
   X(18, 2, 8, 2, 1, 0)   /* block  256 rows: 8 waves x 32            */ \
-  X(19, 2, 4, 2, 2, 0)   /* block  128 rows, 2 workgroups per CU     */
+  X(19, 2, 4, 2, 2, 0)   /* block  128 rows, 2 workgroups per CU     */ \
+  X(20, 4, 4, 4, 1, 0)   /* block  256 rows: 4 waves x 64            */
 
 enum KernelCfg : int32_t {
   CFG_P32 = 0,
@@ -42,6 +43,7 @@ enum KernelCfg : int32_t {
   CFG_P128_W8 = 12,
   CFG_B256 = 18,
   CFG_B128_X2 = 19,
+  CFG_B256_Q4 = 20,
 };
 
 struct CfgInfo {

@@ -212,15 +212,16 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 // Softmax reference: each pass (one split of the prefix, or the block) runs
 // against a fixed per-row reference m, the exact row maxima of its first tile
 // (peeled out of the tile loop); every later tile computes p = exp2(s*c - m)
-// with no max reduction and no rescale of O.  The loop only keeps a lane-local
-// running max of the raw scores; after the last tile the workgroup checks
-// whether any score went more than 2^64 above its row's reference (p must
-// stay far inside the fp32 / bf16 range).  If one did -- rare: it takes a
-// score jump of about 44 nats within one split -- the pass is run again with
-// the exact maxima of the whole split as the reference, which no score can
-// exceed.  The normalised result does not depend on the reference.
+// with no max reduction, no rescale of O and no per-tile check.  Row sums
+// accumulate the bf16-rounded p that the PV product uses (v_dot2), so O and l
+// are normalised consistently.  After the last tile each row's l bounds all of
+// its p: if some l exceeds 2^80 (or is infinite) a score outran the reference
+// by more than about 55 nats within the split -- rare -- and the workgroup
+// finds the split's exact row maxima with a scores-only pass and runs the pass
+// again against them, where no p exceeds 1.  The normalised result does not
+// depend on the reference.
 
-constexpr float kRefMargin = 64.f;   // log2 headroom of scores above the reference
+constexpr float kSumLimit = 1.2089258e24f;   // 2^80: a row sum beyond it sends the pass to the rerun
 
 #define FB_LDS __attribute__((address_space(3)))
 
@@ -283,7 +284,20 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* s
 #ifndef FB_V_AHEAD
 #define FB_V_AHEAD 2
 #endif
+#ifndef FB_K_AHEAD
+#define FB_K_AHEAD 1
+#endif
 constexpr int kVAhead = FB_V_AHEAD;   // V^T fragment groups read ahead of their MFMAs
+constexpr int kKAhead = FB_K_AHEAD;   // K fragment k-steps read ahead of their MFMAs
+#ifndef FB_MFMA_PRIO
+#define FB_MFMA_PRIO 1
+#endif
+// raise the wave's issue priority over its MFMA runs, so the matrix core is
+// fed first when the waves sharing a SIMD are in different phases
+template <int P>
+__device__ __forceinline__ void mfma_prio() {
+  if constexpr (FB_MFMA_PRIO != 0) __builtin_amdgcn_s_setprio(P);
+}
 
 template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL>
 __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
@@ -409,10 +423,12 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
     };
-    kload(0);
+#pragma unroll
+    for (int ks = 0; ks < kKAhead; ++ks) kload(ks);
+    mfma_prio<1>();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) kload(ks + 1);
+      if (ks + kKAhead < KS) kload(ks + kKAhead);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -421,6 +437,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
           s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], qf[qt][ks], s[tt][qt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_prio<0>();
   };
 
   // exact row maxima of the tile (4 lane groups share a query column)
@@ -435,27 +452,29 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     return mx * c;
   };
   // p = exp2(s*c - m) against the reference, packed to bf16 for the PV
-  // product; row sums (this lane's 16 keys) in rs
+  // product; the packed values (this lane's 16 keys of each row) are summed
+  // into l with v_dot2 against (1, 1)
   bf16x8 pf[2][QT];
-  float rs[QT];
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
   auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float msub = m_run[qt] == kNegInf ? 0.f : m_run[qt];
-      float sum = 0.f;
       uint32_t pk[4][2];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][qt][i], c, -msub));
-          sum += p[i];
-        }
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][qt][i], c, -msub));
         pk[tt][0] = pack_bf16x2(p[0], p[1]);
         pk[tt][1] = pack_bf16x2(p[2], p[3]);
       }
-      rs[qt] = sum;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[tt][h]), ones2, l_run[qt], false);
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         u32x4 pv = {pk[2 * jj][0], pk[2 * jj][1], pk[2 * jj + 1][0], pk[2 * jj + 1][1]};
@@ -467,11 +486,12 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // softmax of the scores in s (tile with nvalid keys), then O^T += V^T P^T
   // with V at LDS offset vb.  The PV product runs in NG groups (key half jj,
   // d tile dt), each one V^T fragment (two transpose reads) and QT MFMAs.
-  // FIRST: the pass's first tile, which sets the reference; later tiles feed
-  // the lane-local running max mx_lane instead.
+  // MODE 1: the pass's first tile, which sets the reference; MODE 0: a later
+  // tile; MODE 2: scores only, feeding the lane-local maxima mx_lane (the
+  // rerun's first pass).
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  auto softmax_pv = [&](uint32_t vb, int nvalid, auto first_tag) __attribute__((always_inline)) {
-    constexpr bool FIRST = decltype(first_tag)::value;
+  auto softmax_pv = [&](uint32_t vb, int nvalid, auto mode_tag) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
     bf16x8 vf[NG];
     auto vload = [&](int g) __attribute__((always_inline)) {
       const int jj = g / DT, dt = g % DT;
@@ -480,9 +500,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((FB_LDS bf16x4*)(uintptr_t)(va + 16 * 2 * D));
       vf[g] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
+    if constexpr (MODE != 2) {
 #pragma unroll
-    for (int g = 0; g < kVAhead; ++g) vload(g);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int g = 0; g < kVAhead; ++g) vload(g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (nvalid < kTile) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -494,20 +516,21 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
             if (dead) s[tt][qt][i] = kNegInf;
         }
     }
-    if constexpr (FIRST) {
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) m_run[qt] = row_max(qt);
-    } else {
+    if constexpr (MODE == 2) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx_lane[qt] = fmaxf(mx_lane[qt], s[tt][qt][i]);
+      return;
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) m_run[qt] = row_max(qt);
     }
     exps();
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) l_run[qt] += rs[qt];
+    mfma_prio<1>();
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g + kVAhead < NG) vload(g + kVAhead);
@@ -517,6 +540,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
         oacc[g % DT][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g], pf[g / DT][qt], oacc[g % DT][qt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_prio<0>();
   };
 
   // ---- pipeline: position j of the queue = tile k + j; stage of tile k = st ----
@@ -527,7 +551,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // one tile: wait for it (tiles issued after it may stay in flight), one
   // barrier (every wave is done with the stage refilled next), issue the tile
   // DIST ahead, compute, advance the queue
-  auto tile_step = [&](auto first_tag) __attribute__((always_inline)) {
+  auto tile_step = [&](auto mode_tag) __attribute__((always_inline)) {
     int after = 0;
 #pragma unroll
     for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
@@ -538,7 +562,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     const uint32_t kb = lds0 + st * STAGE;
     if (wave_active) {
       scores(kb);
-      softmax_pv(kb + TBYTES, q_nv[0], first_tag);
+      softmax_pv(kb + TBYTES, q_nv[0], mode_tag);
     }
 #pragma unroll
     for (int j = 0; j < DIST; ++j) {
@@ -549,8 +573,9 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     q_have[DIST] = false;
     st = st + 1 == NS ? 0 : st + 1;
   };
-  // one pass over the tiles of the split; false if it has none
-  auto run_pass = [&](auto first_tag) __attribute__((always_inline)) -> bool {
+  // one pass over the tiles of the split (its first tile in mode first_tag,
+  // the others in mode rest_tag); false if it has none
+  auto run_pass = [&](auto first_tag, auto rest_tag) __attribute__((always_inline)) -> bool {
     st = 0;
 #pragma unroll
     for (int j = 0; j < DIST; ++j) {
@@ -559,33 +584,32 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
     if (!q_have[0]) return false;
     tile_step(first_tag);
-    while (q_have[0]) tile_step(IC<0>{});
+    while (q_have[0]) tile_step(rest_tag);
     return true;
   };
   const TileIter it0 = wk.it;
-  if (run_pass(IC<1>{})) {
-    // did a score outrun its row's reference by more than the margin?
+  if (run_pass(IC<1>{}, IC<0>{})) {
+    // did a score outrun its row's reference?  (l bounds every p of the row)
     bool redo = false;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      float mx = mx_lane[qt];
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      mx_lane[qt] = mx * c;   // exact row maxima over the split
-      redo |= wave_active && mx_lane[qt] > m_run[qt] + kRefMargin;
-    }
+    for (int qt = 0; qt < QT; ++qt) redo |= wave_active && l_run[qt] > kSumLimit;
     if (__any(redo) && lane == 0) wg_redo = 1;
     __syncthreads();
-    if (wg_redo) {   // rare: again, against the split's exact maxima
+    if (wg_redo) {   // rare: the split's exact row maxima, then the pass again against them
+      wk.it = it0;
+      run_pass(IC<2>{}, IC<2>{});
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        m_run[qt] = fmaxf(m_run[qt], mx_lane[qt]);
+        float mx = mx_lane[qt];
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        m_run[qt] = mx * c;
         l_run[qt] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
       wk.it = it0;
-      run_pass(IC<0>{});
+      run_pass(IC<0>{}, IC<0>{});
     }
   }
 
