@@ -240,7 +240,8 @@ def main() -> int:
     # ---- per-step latency: refresh vs reuse steps (first block) ----
     st0 = states[0]
     lat = {"refresh": [], "reuse": []}
-    for rep in range(max(5, args.steps // 2)):
+    n_rep = max(20, args.steps // 2)   # >= 20 refresh steps (one per block pass)
+    for rep in range(n_rep):
         kp, vp = layers[0][rep % N_LAYERS]
         for s in range(w.steps):
             q, k, v = steps_dev[0][s]
@@ -251,6 +252,7 @@ def main() -> int:
             torch.cuda.synchronize()
             lat["refresh" if refreshed else "reuse"].append(e0.elapsed_time(e1) * 1e3)
     med = lambda xs: float(np.median(xs)) if xs else None
+    pct = lambda xs, q: float(np.percentile(xs, q)) if xs else None
 
     # ---- the dominant kernel alone: split-KV prefix pass (fb_prefix_partials) ----
     q0 = steps_dev[0][0][0]
@@ -289,6 +291,18 @@ def main() -> int:
         q, k, v = steps_dev[0][s]
         st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
         drift.append(float((st0.o.float() - full_o[s]).abs().max()))
+
+    sparse_only_drift = None
+    if args.sparse:   # context: the selected chunks alone, without the cached residual
+        o_sel = torch.empty_like(st0.o_ext)
+        l_sel = torch.empty_like(st0.lse_ext)
+        o_so = torch.empty_like(st0.o)
+        sparse_only_drift = []
+        for s in range(w.steps):
+            q, k, v = steps_dev[0][s]
+            fbl.fb_prefix_attn(st0.desc, q, kp, vp, sel, o_sel, l_sel, st0.ws, st0.ws_bytes)
+            fbl.fb_block_attn(st0.desc, q, k, v, o_sel, l_sel, o_so)
+            sparse_only_drift.append(float((o_so.float() - full_o[s]).abs().max()))
 
     lens = block_prefix[0][2]
     lens = [int(lens[b + 1] - lens[b]) for b in range(w.batch)]
@@ -344,12 +358,19 @@ def main() -> int:
         },
         "full_recompute": {"value": q_tokens / (ms_full * 1e-3), "unit": "query-tok/s", "ms_per_step": ms_full},
         "speedup_vs_full": ms_full / ms_cached,
-        "step_latency_us": {"refresh_median": med(lat["refresh"]), "reuse_median": med(lat["reuse"]),
+        "step_latency_us": {"refresh_median": med(lat["refresh"]), "refresh_p10": pct(lat["refresh"], 10),
+                            "refresh_p90": pct(lat["refresh"], 90), "reuse_median": med(lat["reuse"]),
+                            "reuse_p10": pct(lat["reuse"], 10), "reuse_p90": pct(lat["reuse"], 90),
+                            "samples": {"refresh": len(lat["refresh"]), "reuse": len(lat["reuse"])},
                             "launch_floor": ms_floor * 1e3},
+        "block_pass": {"us": ms_block * 1e3, "algorithmic_bytes": bb, "algorithmic_flops": bf,
+                       "gbs": bb / (ms_block * 1e-3) / 1e9, "tflops": bf / (ms_block * 1e-3) / 1e12,
+                       "mfma_frac": bf / (ms_block * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels_us": {"prefix_splitkv": ms_prefix_kernel * 1e3, "split_combine": ms_combine * 1e3,
                        "block_attn_merge": ms_block * 1e3},
         "drift_max_abs": max(drift),
         "drift_per_step": drift,
+        "sparse_only_drift_max_abs": max(sparse_only_drift) if sparse_only_drift else None,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -155,7 +155,7 @@ fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len
   for (int b = 0; b < d->batch; ++b) total_tiles += logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles);
   // Smallest split length whose workgroups all fit in one resident round
   // (capacity = CUs x workgroups per CU): a second, partly filled round would
-  // double the pass time.  Splits of at least kMinSplitTiles tiles.
+  // double the pass time.  Splits of at least kMinSplitTiles tiles (bf16).
   const int64_t capacity = (int64_t)kCUs * ci.wgs_per_cu;
   int64_t max_tiles = 0;
   for (int b = 0; b < d->batch; ++b)
@@ -165,9 +165,11 @@ fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len
     for (int b = 0; b < d->batch; ++b) n += ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles), st_);
     return n * units;
   };
-  int64_t st = std::max<int64_t>(kMinSplitTiles, ceil_div(total_tiles * units, capacity));
+  // (the fp32 kernel runs one wave per workgroup and gains from splits of one tile)
+  const int64_t min_split = d->dtype == FB_F32 ? 1 : kMinSplitTiles;
+  int64_t st = std::max<int64_t>(min_split, ceil_div(total_tiles * units, capacity));
   while (st < max_tiles && wgs_for(st) > capacity) ++st;
-  st = std::max<int64_t>(st, kMinSplitTiles);
+  st = std::max<int64_t>(st, min_split);
   if (st > (1 << 28)) st = 1 << 28;
   p->split_tiles = (int)st;
   int64_t splits = 0;

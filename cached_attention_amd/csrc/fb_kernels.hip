@@ -704,18 +704,39 @@ __global__ void __launch_bounds__(64) attn_f32(const AttnArgs a) {
     }
     __syncthreads();
     if (!active) continue;
-    for (int t = 0; t < nvalid; ++t) {
-      float s = 0.f;
+    // KG keys at a time: KG independent dot-product chains, one rescale per group
+    constexpr int KG = 8;
+    for (int t = 0; t < nvalid; t += KG) {
+      float sc[KG];
 #pragma unroll
-      for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], Kt[t][d], s);
-      const float ts = s * c;
-      const float m_new = fmaxf(m_run, ts);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      const float p = __builtin_amdgcn_exp2f(ts - m_new);
+      for (int j = 0; j < KG; ++j) sc[j] = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int j = 0; j < KG; ++j) sc[j] = __builtin_fmaf(q[d], Kt[t + j][d], sc[j]);
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        sc[j] = t + j < nvalid ? sc[j] * c : kNegInf;
+        mx = fmaxf(mx, sc[j]);
+      }
+      const float m_new = fmaxf(m_run, mx);   // finite: key t is valid
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+      float p[KG], ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(sc[j] - m_new);
+        ps += p[j];
+      }
       m_run = m_new;
-      l_run = l_run * alpha + p;
+      l_run = l_run * alpha + ps;
 #pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(p, Vt[t][d], acc[d] * alpha);
+      for (int d = 0; d < D; ++d) {
+        float a_d = acc[d] * alpha;
+#pragma unroll
+        for (int j = 0; j < KG; ++j) a_d = __builtin_fmaf(p[j], Vt[t + j][d], a_d);
+        acc[d] = a_d;
+      }
     }
   }
   if (!active) return;
