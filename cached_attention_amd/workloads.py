@@ -188,6 +188,48 @@ def make_block_steps(w: Workload, rng: np.random.Generator) -> BlockSteps:
     return BlockSteps(q, k, v)
 
 
+def make_block_steps_decoding(w: Workload, rng: np.random.Generator, head_spread: float = 0.0) -> BlockSteps:
+    """Block steps that imitate progressive unmasking, for the adaptive reuse policies.
+
+    Step 0 draws every token as in ``make_block_steps``.  The block's Lb tokens
+    are then revealed over steps 1 .. S-1 in seeded, uneven batches (a
+    multinomial split): a revealed token's Q, K and V rows are redrawn once
+    (an abrupt update), every other token takes the random-walk step.  With
+    ``head_spread`` > 0, query head h drifts with sigma * u_h, u_h ~ U[1 -
+    head_spread, 1 + head_spread] (seeded), so heads vary across steps unevenly
+    (the video case of head-wise selection).  Draw order: reveal counts,
+    per-head factors, step 0 tokens, then per step: the revealed set, fresh
+    rows, and the noise for Q, K, V.
+    """
+    steps, lb = w.steps, w.block_len
+    counts = rng.multinomial(lb, [1.0 / max(1, steps - 1)] * max(1, steps - 1)) if steps > 1 else np.zeros(0, int)
+    u = (rng.uniform(1.0 - head_spread, 1.0 + head_spread, size=w.hq).astype(np.float32)
+         if head_spread > 0 else np.ones(w.hq, dtype=np.float32))
+    qs = (w.batch, lb, w.hq, w.head_dim)
+    ks = (w.batch, lb, w.hkv, w.head_dim)
+    q = np.empty((steps,) + qs, dtype=np.float32)
+    k = np.empty((steps,) + ks, dtype=np.float32)
+    v = np.empty((steps,) + ks, dtype=np.float32)
+    q[0] = _draw(rng, qs, w.value_scale, w.dtype)
+    k[0] = _draw(rng, ks, w.value_scale, w.dtype)
+    v[0] = _draw(rng, ks, w.value_scale, w.dtype)
+    hidden = np.arange(lb)
+    sig = np.float32(w.drift_sigma)
+    for s in range(1, steps):
+        n = int(counts[s - 1])
+        reveal = rng.choice(hidden, size=min(n, len(hidden)), replace=False) if n > 0 else np.zeros(0, int)
+        hidden = np.setdiff1d(hidden, reveal)
+        fq, fk, fv = (_draw(rng, (w.batch, len(reveal)) + sh[2:], w.value_scale, w.dtype) for sh in (qs, ks, ks))
+        eq = rng.standard_normal(size=qs, dtype=np.float32) * (sig * u)[None, None, :, None]
+        ek = rng.standard_normal(size=ks, dtype=np.float32) * sig
+        ev = rng.standard_normal(size=ks, dtype=np.float32) * sig
+        for arr, eps_, fresh in ((q, eq, fq), (k, ek, fk), (v, ev, fv)):
+            nxt = arr[s - 1] + eps_
+            nxt[:, reveal] = fresh
+            arr[s] = round_bf16(nxt) if w.dtype == "bf16" else nxt
+    return BlockSteps(q, k, v)
+
+
 def make_chunk_selection(w: Workload, prefix_lengths: List[int], seed_offset: int = 1000) -> np.ndarray:
     """Seeded stand-in for a sparse-attention chunk selector.
 

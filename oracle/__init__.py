@@ -18,7 +18,10 @@ Pins (tests/test_oracle_pins.py): brute force on tiny inputs, the CPU fp64
 own GQA convention), hand-derived worked examples under ``tests/golden/``,
 closed forms (zero keys, constant values, a single key, score shifts, key
 permutations), the partition invariant of the merge, cached mode at r = 1
-against full recompute, and the refresh schedule.  Cached mode at r > 1 is an
+against full recompute, and the refresh schedule.  The adaptive reuse policies
+(``policies.py``) are pinned by constructed update counts and similarities,
+their extreme thresholds against full recompute and against never refreshing,
+and a per-head partition of given masks.  Cached mode at r > 1 is an
 approximation the pages define only as a procedure: its values are pinned only
 through those building blocks ("parity unpinned" for the drift values).
 """
@@ -38,4 +41,11 @@ from .attention import (  # noqa: F401
     sparse_only_step,
     grow_prefix,
     BlockResult,
+)
+from .policies import (  # noqa: F401
+    updated_tokens,
+    tau_mask,
+    head_similarity,
+    gamma_mask,
+    run_block_policy,
 )

@@ -417,3 +417,109 @@ def test_grow_prefix_appends_last_step_block():
     np.testing.assert_array_equal(k2[5:8], kl[0])
     np.testing.assert_array_equal(k2[8:15], k_pre[5:12])
     np.testing.assert_array_equal(v2[15:18], vl[1])
+
+
+# ---------------------------------------------------------------------------
+# adaptive reuse policies (Adaptive Reuse Strategies): tau on updated tokens,
+# head-wise similarity gamma
+# ---------------------------------------------------------------------------
+
+def test_updated_tokens_counts_constructed_changes():
+    b_n, lb, hkv, d = 2, 9, 2, 4
+    eps = 0.25
+    kp = np.zeros((b_n, lb, hkv, d))
+    vp = np.zeros((b_n, lb, hkv, d))
+    kc, vc = kp.copy(), vp.copy()
+    kc[0, 2, 1, 3] = eps + 1e-3        # stream 0: token 2 via K
+    vc[0, 5, 0, 0] = -(eps + 0.5)      # stream 0: token 5 via V, negative change
+    kc[0, 7, 0, 1] = eps               # exactly eps: not an update
+    vc[1, 8, 1, 2] = 3.0               # stream 1: token 8
+    kc[1, 8, 0, 0] = 3.0               # (same token again: counted once)
+    assert oracle.updated_tokens(kp, vp, kc, vc, eps).tolist() == [2, 1]
+    assert oracle.updated_tokens(kp, vp, kp, vp, 0.0).tolist() == [0, 0]
+
+
+def test_tau_mask_rule():
+    m = np.array([3, 9, 5])
+    assert oracle.tau_mask(m, 5, 1, 2).tolist() == [[0, 0], [1, 1], [1, 1]]   # reuse iff M < tau
+    assert oracle.tau_mask(m, 100, 0, 2).tolist() == [[1, 1]] * 3             # step 0 always
+
+
+def test_head_similarity_closed_forms():
+    rng = np.random.default_rng(21)
+    q = _rand(rng, 1, 5, 4, 8)
+    q2 = q.copy()
+    q2[0, :, 0, :] *= 2.5                  # same direction -> 1
+    q2[0, :, 1, :] *= -1.0                 # opposite -> -1
+    x = q[0, :, 2, :].ravel()
+    y = _rand(rng, x.size)
+    y -= x * (np.dot(x, y) / np.dot(x, x))  # orthogonal -> 0
+    q2[0, :, 2, :] = y.reshape(5, 8)
+    q2[0, :, 3, :] = 0.0                   # zero norm -> 0 (refresh)
+    sim = oracle.head_similarity(q, q2)
+    np.testing.assert_allclose(sim[0], [1.0, -1.0, 0.0, 0.0], atol=1e-12)
+
+
+def test_gamma_mask_groups_and_threshold():
+    sim = np.array([[0.99, 0.5, 0.99, 0.99], [0.95, 0.95, 0.91, 0.9]])
+    # hq 4, hkv 2: heads {0,1} -> KV 0, {2,3} -> KV 1; refresh iff sim <= gamma
+    assert oracle.gamma_mask(sim, 0.9, 1, 4, 2).tolist() == [[1, 0], [0, 1]]
+    assert oracle.gamma_mask(sim, 0.0, 0, 4, 2).tolist() == [[1, 1], [1, 1]]
+
+
+def _decoding_block(seed=31, steps=5, lp=130, hq=4, hkv=2, head_spread=0.0):
+    w = wl.Workload("p", "f32", 2, hq, hkv, 16, 12, lp, steps, 1.0, 0.05, ragged=0.25, seed=seed)
+    rng = np.random.default_rng(seed)
+    prefix = wl.make_prefix(w, rng)
+    return w, prefix, wl.make_block_steps_decoding(w, rng, head_spread)
+
+
+@pytest.mark.parametrize("policy", ["tau", "gamma"])
+def test_policy_extremes_equal_full_and_never(policy):
+    """Always-recompute thresholds reproduce full recompute; never-recompute ones
+    reproduce the cache of step 0 kept for the whole block (r > S)."""
+    w, p, blk = _decoding_block()
+    scale = 1 / math.sqrt(w.head_dim)
+    args = dict(k_pre=p.k, v_pre=p.v, offsets=p.offsets, q_steps=blk.q, k_steps=blk.k, v_steps=blk.v,
+                scale=scale, policy=policy)
+    always = dict(tau=0, eps=0.1) if policy == "tau" else dict(gamma=2.0)
+    never = dict(tau=w.block_len + 1, eps=0.1) if policy == "tau" else dict(gamma=-2.0)
+    full = oracle.run_block(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, mode="full")
+    keep = oracle.run_block(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, r=w.steps + 1)
+    a = oracle.run_block_policy(**args, **always)
+    n = oracle.run_block_policy(**args, **never)
+    for s in range(w.steps):
+        np.testing.assert_allclose(a.out[s], full.out[s], rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(n.out[s], keep.out[s])
+        assert a.masks[s].all() and (n.masks[s].all() if s == 0 else not n.masks[s].any())
+
+
+def test_policy_given_masks_partition_heads():
+    """A constant mask after step 0: query heads of recomputed KV heads match full
+    recompute, the others match the step-0 cache kept (r > S), head by head."""
+    w, p, blk = _decoding_block(hq=6, hkv=3)
+    scale = 1 / math.sqrt(w.head_dim)
+    pattern = np.array([[1, 0, 1], [0, 1, 0]], dtype=np.int32)
+    masks = [np.ones((2, 3), np.int32)] + [pattern] * (w.steps - 1)
+    got = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, "given", masks=masks)
+    full = oracle.run_block(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, mode="full")
+    keep = oracle.run_block(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, r=w.steps + 1)
+    for s in range(1, w.steps):
+        for b in range(2):
+            for h in range(6):
+                ref = full.out[s] if pattern[b, h // 2] else keep.out[s]
+                np.testing.assert_allclose(got.out[s][b, :, h], ref[b, :, h], rtol=0, atol=1e-12)
+
+
+def test_tau_policy_counts_follow_reveals():
+    """Decoding-style steps: M equals the tokens revealed at each step (the other
+    tokens drift by sigma 0.05, far below eps 0.5), and the mask follows tau."""
+    w, p, blk = _decoding_block(steps=6)
+    scale = 1 / math.sqrt(w.head_dim)
+    got = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, scale, "tau", tau=3, eps=0.5)
+    rng = np.random.default_rng(31)
+    wl.make_prefix(w, rng)
+    counts = rng.multinomial(w.block_len, [1.0 / (w.steps - 1)] * (w.steps - 1))
+    for s in range(1, w.steps):
+        assert got.counts[s].tolist() == [counts[s - 1]] * 2
+        assert got.masks[s].tolist() == [[int(counts[s - 1] >= 3)] * 2] * 2
