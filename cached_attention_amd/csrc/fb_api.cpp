@@ -12,6 +12,8 @@
 #include "fb_internal.h"
 #include "flashblock.h"
 
+static_assert(fb::kDtypeBf16 == FB_BF16, "dtype tag of the kernels");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -214,7 +216,8 @@ fb_status hip_status(int err, const char* what) {
 // The two halves of the prefix pass for a chosen chunk mode.  Both derive the
 // same plan (and so the same workspace layout) from (d, chunk mode, sp).
 fb_status run_partials(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
-                       const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream) {
+                       const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream,
+                       const int32_t* head_mask = nullptr) {
   PrefixPlan p;
   const int n_sel = sp ? sp->k : 0;
   fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
@@ -238,12 +241,13 @@ fb_status run_partials(const fb_desc* d, const void* q, const void* k_pre, const
   a.chunk_mode = chunk_mode;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + p.part_o_bytes);
+  a.head_mask = head_mask;
   return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, p.cfg, true, stream), "prefix attention launch");
 }
 
 fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, const float* extra_o,
                       const float* extra_lse, float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes,
-                      void* stream) {
+                      void* stream, const int32_t* head_mask = nullptr) {
   PrefixPlan p;
   const int n_sel = sp ? sp->k : 0;
   fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
@@ -268,16 +272,19 @@ fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, con
   c.extra_lse = extra_lse;
   c.o = o_ext;
   c.lse = lse_ext;
+  c.head_mask = head_mask;
+  c.Hkv = d->hkv;
+  c.G = d->hq / d->hkv;
   const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
   return hip_status(fb::launch_combine(c, rows, stream), "split combine launch");
 }
 
 fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
                      const fb_sparse* sp, const float* extra_o, const float* extra_lse, float* o_ext,
-                     float* lse_ext, void* ws, size_t ws_bytes, void* stream) {
-  fb_status st = run_partials(d, q, k_pre, v_pre, chunk_mode, sp, ws, ws_bytes, stream);
+                     float* lse_ext, void* ws, size_t ws_bytes, void* stream, const int32_t* head_mask = nullptr) {
+  fb_status st = run_partials(d, q, k_pre, v_pre, chunk_mode, sp, ws, ws_bytes, stream, head_mask);
   if (st != FB_OK) return st;
-  return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream);
+  return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream, head_mask);
 }
 
 fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const void* v_blk, const float* o_ext,
@@ -316,6 +323,7 @@ size_t workspace_for(const fb_desc* d, const fb_sparse* sp) {
       need = std::max(need, p.part_o_bytes + p.part_lse_bytes);
     }
   }
+  need = std::max(need, (size_t)d->batch * d->block_len * sizeof(int32_t));   // fb_refresh_mask_tau flags
   return std::max<size_t>(need, kAlign);
 }
 
@@ -477,6 +485,94 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
                     lse_ext_cache, ws, ws_bytes, stream);
     if (st != FB_OK) return st;
   }
+  return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
+}
+
+fb_status fb_refresh_mask_tau(const fb_desc* d, const void* k_prev, const void* v_prev, const void* k_cur,
+                              const void* v_cur, float eps, int32_t tau, int32_t step, int32_t* count_out,
+                              int32_t* mask_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st != FB_OK) return st;
+  if (step < 0) return fail(FB_ERR_ARG, "step = %d < 0", step);
+  if (!(eps >= 0.f)) return fail(FB_ERR_ARG, "eps must be >= 0");
+  if (!count_out || !mask_out) return fail(FB_ERR_NULL, "count_out and mask_out are required");
+  if (step > 0 && (!k_prev || !v_prev || !k_cur || !v_cur))
+    return fail(FB_ERR_NULL, "k_prev, v_prev, k_cur and v_cur are required after step 0");
+  const size_t need = (size_t)d->batch * d->block_len * sizeof(int32_t);
+  if (ws_bytes < need) return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!ws) return fail(FB_ERR_NULL, "workspace is NULL");
+  fb::TauArgs t;
+  memset(&t, 0, sizeof(t));
+  t.k_prev = k_prev;   // not read at step 0, where every token counts as new
+  t.v_prev = v_prev;
+  t.k_cur = k_cur;
+  t.v_cur = v_cur;
+  t.kv_sb = d->kv_stride_b;
+  t.kv_st = d->kv_stride_t;
+  t.kv_sh = d->kv_stride_h;
+  t.B = d->batch;
+  t.Lb = d->block_len;
+  t.Hkv = d->hkv;
+  t.D = d->head_dim;
+  t.dtype = d->dtype;
+  t.eps = eps;
+  t.tau = tau;
+  t.step = step;
+  t.flags = (int32_t*)ws;
+  t.count = count_out;
+  t.mask = mask_out;
+  return hip_status(fb::launch_tau(t, stream), "tau mask launch");
+}
+
+fb_status fb_refresh_mask_gamma(const fb_desc* d, const void* q_cur, void* q_ref, float gamma, int32_t step,
+                                float* sim_out, int32_t* mask_out, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st != FB_OK) return st;
+  if (step < 0) return fail(FB_ERR_ARG, "step = %d < 0", step);
+  if (gamma != gamma) return fail(FB_ERR_ARG, "gamma is NaN");
+  if (!q_cur || !q_ref || !sim_out || !mask_out)
+    return fail(FB_ERR_NULL, "q_cur, q_ref, sim_out and mask_out are required");
+  fb::GammaArgs g;
+  memset(&g, 0, sizeof(g));
+  g.q_cur = q_cur;
+  g.q_sb = d->q_stride_b;
+  g.q_st = d->q_stride_t;
+  g.q_sh = d->q_stride_h;
+  g.q_ref = q_ref;
+  g.B = d->batch;
+  g.Lb = d->block_len;
+  g.Hq = d->hq;
+  g.Hkv = d->hkv;
+  g.D = d->head_dim;
+  g.dtype = d->dtype;
+  g.gamma = gamma;
+  g.step = step;
+  g.sim = sim_out;
+  g.mask = mask_out;
+  return hip_status(fb::launch_gamma(g, stream), "gamma mask launch");
+}
+
+fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                         const void* k_pre, const void* v_pre, const int32_t* mask, float* o_ext_cache,
+                         float* lse_ext_cache, void* o, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st != FB_OK) return st;
+  if (!q_blk || !k_blk || !v_blk || !mask || !o_ext_cache || !lse_ext_cache || !o)
+    return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk, mask, o_ext_cache, lse_ext_cache and o are required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pre) || !aligned16(v_pre) ||
+      !aligned16(o_ext_cache) || !aligned16(o))
+    return fail(FB_ERR_ALIGN, "all tensor base pointers must be 16-byte aligned");
+  st = check_ws(ws, ws_bytes, workspace_for(d, nullptr));
+  if (st != FB_OK) return st;
+  st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_ALL, nullptr, nullptr, nullptr, o_ext_cache, lse_ext_cache,
+                  ws, ws_bytes, stream, mask);
+  if (st != FB_OK) return st;
   return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
 }
 

@@ -8,6 +8,7 @@ namespace fb {
 enum ChunkMode : int32_t { CHUNKS_ALL = 0, CHUNKS_SELECTED = 1, CHUNKS_COMPLEMENT = 2 };
 
 constexpr int kTile = 64;  // keys per LDS tile
+constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
 
 // bf16 kernel configurations.  X(id, rows per wave / 16, waves, LDS stages,
 // resident workgroups per CU, pass: 1 = split partial of the prefix pass,
@@ -87,6 +88,9 @@ struct AttnArgs {
   const float* ext_lse;
   void* o;
   float* lse_out;
+  // per-(stream, KV head) recompute mask [B][Hkv] (nullable = all): workgroups
+  // of a masked-out head exit at once
+  const int32_t* head_mask;
 };
 
 struct CombineArgs {
@@ -100,6 +104,33 @@ struct CombineArgs {
   const float* extra_lse;
   float* o;                // [B][Hq][Lb][D]
   float* lse;              // [B][Hq][Lb]
+  const int32_t* head_mask;  // [B][Hkv] (nullable = all): rows of masked-out heads are left untouched
+  int32_t Hkv, G;
+};
+
+// Adaptive reuse masks.
+struct TauArgs {
+  const void* k_prev;
+  const void* v_prev;
+  const void* k_cur;
+  const void* v_cur;
+  int64_t kv_sb, kv_st, kv_sh;
+  int32_t B, Lb, Hkv, D, dtype;
+  float eps;
+  int32_t tau, step;
+  int32_t* flags;    // [B][Lb] scratch
+  int32_t* count;    // [B]
+  int32_t* mask;     // [B][Hkv]
+};
+struct GammaArgs {
+  const void* q_cur;
+  int64_t q_sb, q_st, q_sh;
+  void* q_ref;       // [B][Lb][Hq][D] contiguous, same dtype
+  int32_t B, Lb, Hq, Hkv, D, dtype;
+  float gamma;
+  int32_t step;
+  float* sim;        // [B][Hq]
+  int32_t* mask;     // [B][Hkv]
 };
 
 // launchers (fb_kernels.hip); return hipError_t as int
@@ -107,5 +138,7 @@ int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partia
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream);
 int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* la, const float* ob,
                  const float* lb, float* o, float* lse, void* stream);
+int launch_tau(const TauArgs& t, void* stream);
+int launch_gamma(const GammaArgs& g, void* stream);
 
 }  // namespace fb

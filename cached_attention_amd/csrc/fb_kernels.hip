@@ -319,6 +319,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 
   Work wk;
   if (!decode_work<2>(a, wk)) return;
+  if (a.head_mask && ld_const(a.head_mask, (int64_t)wk.b * a.Hkv + wk.g) == 0) return;   // cache reused
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -668,6 +669,7 @@ __global__ void __launch_bounds__(64) attn_f32(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Vt[kTile][D];
   Work wk;
   if (!decode_work<4>(a, wk)) return;
+  if (a.head_mask && ld_const(a.head_mask, (int64_t)wk.b * a.Hkv + wk.g) == 0) return;   // cache reused
   const int lane = threadIdx.x;
   const int row = wk.rt * 64 + lane;
   const bool active = row < a.rows;
@@ -781,6 +783,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64
   const int64_t hl = (int64_t)c.Hq * c.Lb;
   const int b = (int)(row / hl);
   const int64_t rem = row % hl;
+  if (c.head_mask && ld_const(c.head_mask, (int64_t)b * c.Hkv + (int)(rem / c.Lb) / c.G) == 0) return;
   int x0 = 0;
   for (int bb = 0; bb < b; ++bb) x0 += splits_of(c.offsets, bb, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
   int ns = splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
@@ -875,6 +878,122 @@ __global__ void __launch_bounds__(256) merge_kernel(int64_t rows, int D, const f
 }
 
 // ---------------------------------------------------------------------------
+// adaptive reuse masks (FlashBlock explainer page, "Adaptive Reuse Strategies")
+// ---------------------------------------------------------------------------
+//
+// Masks are [B][Hkv] int32, 1 = recompute that (stream, KV head)'s
+// block-external partial at this step.  They stay on the device: the prefix
+// pass and the split combine read them, so no host round trip decides a step.
+
+__device__ __forceinline__ float ld_elem(const void* p, int64_t i, int dtype) {
+  return dtype == kDtypeBf16 ? (float)((const __bf16*)p)[i] : ((const float*)p)[i];
+}
+
+// threshold-based reuse, part 1: one wave per block token -- did its K or V
+// row (any KV head, any dim) change by more than eps since the previous step?
+__global__ void __launch_bounds__(256) tau_flags_kernel(const TauArgs t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= (int64_t)t.B * t.Lb) return;
+  if (t.step == 0) {   // no previous step: every token is new
+    if (lane == 0) t.flags[tok] = 1;
+    return;
+  }
+  const int b = (int)(tok / t.Lb);
+  const int pos = (int)(tok % t.Lb);
+  const int64_t base = (int64_t)b * t.kv_sb + (int64_t)pos * t.kv_st;
+  const int per = t.Hkv * t.D;
+  bool changed = false;
+  for (int e = lane; e < per; e += 64) {
+    const int64_t i = base + (int64_t)(e / t.D) * t.kv_sh + e % t.D;
+    const float dk = fabsf(ld_elem(t.k_cur, i, t.dtype) - ld_elem(t.k_prev, i, t.dtype));
+    const float dv = fabsf(ld_elem(t.v_cur, i, t.dtype) - ld_elem(t.v_prev, i, t.dtype));
+    changed |= dk > t.eps || dv > t.eps;
+  }
+  changed = __any(changed);
+  if (lane == 0) t.flags[tok] = changed ? 1 : 0;
+}
+
+// threshold-based reuse, part 2: one workgroup per stream -- M = updated
+// tokens; recompute every KV head of the stream iff M >= tau (or step 0)
+__global__ void __launch_bounds__(256) tau_finalize_kernel(const TauArgs t) {
+  __shared__ int part[4];
+  const int b = blockIdx.x;
+  int m = 0;
+  for (int i = threadIdx.x; i < t.Lb; i += 256) m += t.flags[(int64_t)b * t.Lb + i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m += __shfl_xor(m, o, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const int total = part[0] + part[1] + part[2] + part[3];
+  const int refresh = (t.step == 0 || total >= t.tau) ? 1 : 0;
+  if (threadIdx.x == 0) t.count[b] = total;
+  for (int g = threadIdx.x; g < t.Hkv; g += 256) t.mask[(int64_t)b * t.Hkv + g] = refresh;
+}
+
+// head-wise selection: one workgroup per (stream, KV head).  For each query
+// head of the group, the cosine similarity of its block queries at the
+// reference step (q_ref) and now (fp64 sums, so the threshold decision does
+// not hinge on fp32 summation order); the KV head is recomputed iff some
+// similarity is <= gamma (or step 0), and then the group's q_ref rows take
+// the current queries.
+__global__ void __launch_bounds__(256) gamma_kernel(const GammaArgs a) {
+  __shared__ double red[3][4];
+  const int b = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int n = a.Lb * a.D;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  bool refresh = a.step == 0;
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    double dot = 0.0, n1 = 0.0, n2 = 0.0;
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int pos = e / a.D, dd = e % a.D;
+      const double x = ld_elem(a.q_ref, (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + dd, a.dtype);
+      const double y = ld_elem(a.q_cur, (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + dd,
+                               a.dtype);
+      dot += x * y;
+      n1 += x * x;
+      n2 += y * y;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      dot += __shfl_xor(dot, o, 64);
+      n1 += __shfl_xor(n1, o, 64);
+      n2 += __shfl_xor(n2, o, 64);
+    }
+    if (lane == 0) {
+      red[0][wave] = dot;
+      red[1][wave] = n1;
+      red[2][wave] = n2;
+    }
+    __syncthreads();
+    const double sd = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const double s1 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const double s2 = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    const double sim = (s1 > 0.0 && s2 > 0.0) ? sd / sqrt(s1 * s2) : 0.0;
+    if (threadIdx.x == 0) a.sim[(int64_t)b * a.Hq + h] = (float)sim;
+    refresh |= !(sim > (double)a.gamma);
+    __syncthreads();   // red is reused by the next head
+  }
+  if (threadIdx.x == 0) a.mask[(int64_t)b * a.Hkv + g] = refresh ? 1 : 0;
+  if (!refresh) return;
+  const int esz = a.dtype == kDtypeBf16 ? 2 : 4;
+  for (int e = threadIdx.x; e < G * n; e += 256) {
+    const int hh = e / n, r = e % n;
+    const int h = g * G + hh, pos = r / a.D, dd = r % a.D;
+    const int64_t src = (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + dd;
+    const int64_t dst = (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + dd;
+    if (esz == 2)
+      ((__bf16*)a.q_ref)[dst] = ((const __bf16*)a.q_cur)[src];
+    else
+      ((float*)a.q_ref)[dst] = ((const float*)a.q_cur)[src];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -929,6 +1048,20 @@ int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* l
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, head_dim, oa, la,
                      ob, lb, o, lse);
+  return (int)hipGetLastError();
+}
+
+int launch_tau(const TauArgs& t, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t toks = (int64_t)t.B * t.Lb;
+  hipLaunchKernelGGL(tau_flags_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, t);
+  hipLaunchKernelGGL(tau_finalize_kernel, dim3((unsigned)t.B), dim3(256), 0, s, t);
+  return (int)hipGetLastError();
+}
+
+int launch_gamma(const GammaArgs& g, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)((int64_t)g.B * g.Hkv)), dim3(256), 0, s, g);
   return (int)hipGetLastError();
 }
 

@@ -24,8 +24,8 @@ FB_MODE_CACHED, FB_MODE_FULL = 0, 1
 FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 
 EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
-           "fb_block_attn", "fb_merge", "fb_step",
-           "fb_status_string", "fb_last_error", "fb_abi_version")
+           "fb_block_attn", "fb_merge", "fb_step", "fb_refresh_mask_tau", "fb_refresh_mask_gamma",
+           "fb_step_masked", "fb_status_string", "fb_last_error", "fb_abi_version")
 
 
 class FlashBlockError(RuntimeError):
@@ -88,6 +88,13 @@ def lib() -> ctypes.CDLL:
         l.fb_step.argtypes = [D, P, P, P, P, P, S, P, P, P, P, P, P, i32, i32, i32, i32,
                               ctypes.POINTER(i32), P, sz, P]
         l.fb_step.restype = i32
+        f32 = ctypes.c_float
+        l.fb_refresh_mask_tau.argtypes = [D, P, P, P, P, f32, i32, i32, P, P, P, sz, P]
+        l.fb_refresh_mask_tau.restype = i32
+        l.fb_refresh_mask_gamma.argtypes = [D, P, P, f32, i32, P, P, P]
+        l.fb_refresh_mask_gamma.restype = i32
+        l.fb_step_masked.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        l.fb_step_masked.restype = i32
         l.fb_status_string.argtypes = [i32]
         l.fb_status_string.restype = ctypes.c_char_p
         l.fb_last_error.argtypes = []
@@ -211,6 +218,26 @@ def fb_step(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, sparse: Optional[Spar
                          int(bool(force_refresh)), ctypes.byref(refreshed), _ptr(ws), ws_bytes,
                          _stream(stream)), "fb_step")
     return bool(refreshed.value)
+
+
+def fb_refresh_mask_tau(desc: Desc, k_prev, v_prev, k_cur, v_cur, eps: float, tau: int, step: int, count_out,
+                        mask_out, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().fb_refresh_mask_tau(desc.ref, _ptr(k_prev), _ptr(v_prev), _ptr(k_cur), _ptr(v_cur), eps, tau,
+                                     step, _ptr(count_out), _ptr(mask_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "fb_refresh_mask_tau")
+
+
+def fb_refresh_mask_gamma(desc: Desc, q_cur, q_ref, gamma: float, step: int, sim_out, mask_out,
+                          stream=None) -> None:
+    _check(lib().fb_refresh_mask_gamma(desc.ref, _ptr(q_cur), _ptr(q_ref), gamma, step, _ptr(sim_out),
+                                       _ptr(mask_out), _stream(stream)), "fb_refresh_mask_gamma")
+
+
+def fb_step_masked(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, mask, o_ext_cache, lse_ext_cache, o,
+                   lse_out, ws, ws_bytes: int, stream=None) -> None:
+    _check(lib().fb_step_masked(desc.ref, _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre),
+                                _ptr(mask), _ptr(o_ext_cache), _ptr(lse_ext_cache), _ptr(o), _ptr(lse_out),
+                                _ptr(ws), ws_bytes, _stream(stream)), "fb_step_masked")
 
 
 def fb_status_string(status: int) -> str:

@@ -188,7 +188,8 @@ def make_block_steps(w: Workload, rng: np.random.Generator) -> BlockSteps:
     return BlockSteps(q, k, v)
 
 
-def make_block_steps_decoding(w: Workload, rng: np.random.Generator, head_spread: float = 0.0) -> BlockSteps:
+def make_block_steps_decoding(w: Workload, rng: np.random.Generator, head_spread: float = 0.0,
+                              reveal: bool = True) -> BlockSteps:
     """Block steps that imitate progressive unmasking, for the adaptive reuse policies.
 
     Step 0 draws every token as in ``make_block_steps``.  The block's Lb tokens
@@ -197,7 +198,8 @@ def make_block_steps_decoding(w: Workload, rng: np.random.Generator, head_spread
     (an abrupt update), every other token takes the random-walk step.  With
     ``head_spread`` > 0, query head h drifts with sigma * u_h, u_h ~ U[1 -
     head_spread, 1 + head_spread] (seeded), so heads vary across steps unevenly
-    (the video case of head-wise selection).  Draw order: reveal counts,
+    (the video case of head-wise selection); ``reveal=False`` keeps only the
+    drift (every token changes a little, none abruptly).  Draw order: reveal counts,
     per-head factors, step 0 tokens, then per step: the revealed set, fresh
     rows, and the noise for Q, K, V.
     """
@@ -216,16 +218,16 @@ def make_block_steps_decoding(w: Workload, rng: np.random.Generator, head_spread
     hidden = np.arange(lb)
     sig = np.float32(w.drift_sigma)
     for s in range(1, steps):
-        n = int(counts[s - 1])
-        reveal = rng.choice(hidden, size=min(n, len(hidden)), replace=False) if n > 0 else np.zeros(0, int)
-        hidden = np.setdiff1d(hidden, reveal)
-        fq, fk, fv = (_draw(rng, (w.batch, len(reveal)) + sh[2:], w.value_scale, w.dtype) for sh in (qs, ks, ks))
+        n = int(counts[s - 1]) if reveal else 0
+        shown = rng.choice(hidden, size=min(n, len(hidden)), replace=False) if n > 0 else np.zeros(0, int)
+        hidden = np.setdiff1d(hidden, shown)
+        fq, fk, fv = (_draw(rng, (w.batch, len(shown)) + sh[2:], w.value_scale, w.dtype) for sh in (qs, ks, ks))
         eq = rng.standard_normal(size=qs, dtype=np.float32) * (sig * u)[None, None, :, None]
         ek = rng.standard_normal(size=ks, dtype=np.float32) * sig
         ev = rng.standard_normal(size=ks, dtype=np.float32) * sig
         for arr, eps_, fresh in ((q, eq, fq), (k, ek, fk), (v, ev, fv)):
             nxt = arr[s - 1] + eps_
-            nxt[:, reveal] = fresh
+            nxt[:, shown] = fresh
             arr[s] = round_bf16(nxt) if w.dtype == "bf16" else nxt
     return BlockSteps(q, k, v)
 

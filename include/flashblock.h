@@ -105,8 +105,8 @@ typedef struct fb_sparse {
   int32_t mode;                 /* FB_CHUNKS_SELECTED or FB_CHUNKS_COMPLEMENT */
 } fb_sparse;
 
-/* Bytes of workspace fb_prefix_attn / fb_step need for this shape (split-KV
- * partials).  `sp` may be NULL (dense prefix).  For fb_step in sparse mode pass
+/* Bytes of workspace fb_prefix_attn / fb_step / fb_step_masked /
+ * fb_refresh_mask_tau need for this shape (split-KV partials, tau flags).  `sp` may be NULL (dense prefix).  For fb_step in sparse mode pass
  * the fb_sparse it will get; the larger of the SELECTED and COMPLEMENT plans is
  * returned.  Returns 0 on invalid arguments (see fb_last_error()). */
 size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp);
@@ -172,6 +172,43 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
                   float* lse_res_cache, void* o, float* lse_out, int32_t step,
                   int32_t refresh_period, int32_t mode, int32_t force_refresh,
                   int32_t* refreshed_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Adaptive reuse (explainer page, "Adaptive Reuse Strategies"): instead of a
+ * fixed refresh period, decide per step and per (stream, KV head) whether the
+ * block-external partial is recomputed, entirely on the device.  A mask is
+ * int32 [B][Hkv] in device memory, 1 = recompute at this step, 0 = reuse the
+ * cached partial.  Step 0 of a block always sets every entry to 1.
+ *
+ * fb_refresh_mask_tau: threshold-based reuse.  M = the number of a stream's
+ * block tokens whose K or V row (any KV head, any dim) differs from the
+ * previous step's by more than eps (max-abs); every KV head of the stream is
+ * recomputed iff M >= tau (the cache is reused while M < tau).  k_prev/v_prev
+ * are the previous step's block K/V in the fb_desc block layout (not read at
+ * step 0).  Writes count_out [B] (M; Lb at step 0) and mask_out [B][Hkv].  ws
+ * holds B*Lb int32 flags (fb_workspace_size covers it).
+ *
+ * fb_refresh_mask_gamma: head-wise selection.  For each query head, the cosine
+ * similarity (fp64 sums) of its block queries at the reference step (q_ref,
+ * [B][Lb][Hq][D] contiguous, input dtype, caller-owned) and now (q_cur, fb_desc
+ * q layout); 0 if a norm is 0.  KV head g is recomputed iff some query head of
+ * its group has similarity <= gamma (it is reused only if all exceed gamma);
+ * the group's q_ref rows then take the current queries.  Writes sim_out
+ * [B][Hq] fp32 and mask_out.  At step 0 q_ref may hold anything.
+ *
+ * fb_step_masked: one dense step under a mask: the prefix pass and split
+ * combine run only for the (stream, KV head) pairs the mask selects (the
+ * others' workgroups exit at once and their rows of o_ext_cache / lse_ext_cache
+ * stay as they are), then the in-block pass merges with the cache for every
+ * head into o.  The mask is read on the device, so no host synchronisation is
+ * needed between the mask call and the step. */
+fb_status fb_refresh_mask_tau(const fb_desc* d, const void* k_prev, const void* v_prev, const void* k_cur,
+                              const void* v_cur, float eps, int32_t tau, int32_t step, int32_t* count_out,
+                              int32_t* mask_out, void* ws, size_t ws_bytes, void* stream);
+fb_status fb_refresh_mask_gamma(const fb_desc* d, const void* q_cur, void* q_ref, float gamma, int32_t step,
+                                float* sim_out, int32_t* mask_out, void* stream);
+fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                         const void* k_pre, const void* v_pre, const int32_t* mask, float* o_ext_cache,
+                         float* lse_ext_cache, void* o, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 const char* fb_status_string(fb_status s);
 const char* fb_last_error(void);

@@ -123,3 +123,30 @@ def test_desc_struct_layout():
     assert fbl.fb_desc.prefix_offsets_host.offset == 32
     assert fbl.fb_desc.q_stride_b.offset == 48
     assert ctypes.sizeof(fbl.fb_sparse) == 24
+
+
+def test_adaptive_reuse_validation():
+    d = _desc()
+    lib = fbl.lib()
+    ws_b = fbl.fb_workspace_size(d)
+    tau = lambda **kw: lib.fb_refresh_mask_tau(
+        kw.get("d", d.ref), FAKE, FAKE, FAKE, FAKE, kw.get("eps", 0.1), 3, kw.get("step", 1),
+        kw.get("cnt", FAKE), kw.get("mask", FAKE), kw.get("ws", FAKE), kw.get("wsb", ws_b), None)
+    assert tau(d=None) == fbl.FB_ERR_NULL
+    assert tau(step=-1) == fbl.FB_ERR_ARG
+    assert tau(eps=-1.0) == fbl.FB_ERR_ARG
+    assert tau(eps=float("nan")) == fbl.FB_ERR_ARG
+    assert tau(mask=None) == fbl.FB_ERR_NULL
+    assert tau(wsb=1 * 64 * 4 - 1) == fbl.FB_ERR_WORKSPACE   # B * Lb int32 flags
+    assert ws_b >= 1 * 64 * 4
+    gam = lambda **kw: lib.fb_refresh_mask_gamma(kw.get("d", d.ref), FAKE, kw.get("qr", FAKE),
+                                                 kw.get("g", 0.9), kw.get("step", 1), FAKE, FAKE, None)
+    assert gam(d=None) == fbl.FB_ERR_NULL
+    assert gam(qr=None) == fbl.FB_ERR_NULL
+    assert gam(g=float("nan")) == fbl.FB_ERR_ARG
+    assert gam(step=-2) == fbl.FB_ERR_ARG
+    sm = lambda **kw: lib.fb_step_masked(d.ref, kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("mask", FAKE),
+                                         FAKE, FAKE, FAKE, None, kw.get("ws", FAKE), kw.get("wsb", ws_b), None)
+    assert sm(mask=None) == fbl.FB_ERR_NULL
+    assert sm(q=FAKE + 2) == fbl.FB_ERR_ALIGN
+    assert sm(wsb=ws_b - 1) == fbl.FB_ERR_WORKSPACE
