@@ -127,6 +127,15 @@ def main() -> int:
     ap.add_argument("--sparse", action="store_true",
                     help="chunk-sparse variant: cached residual of the unselected 64-token chunks plus a fresh "
                          "partial over the selected ones (workloads with a sparse keep fraction)")
+    ap.add_argument("--policy", choices=("fixed", "tau", "gamma"), default="fixed",
+                    help="refresh policy: fixed period r, or adaptive reuse on decoding-style block steps "
+                         "(tau: updated-token threshold; gamma: per-head query similarity)")
+    ap.add_argument("--tau", type=int, default=0, help="tau policy: recompute iff >= tau tokens updated "
+                    "(default: a quarter of the block)")
+    ap.add_argument("--eps", type=float, default=0.25, help="tau policy: a token is updated if its K or V "
+                    "changed by more than eps")
+    ap.add_argument("--gamma", type=float, default=0.99, help="gamma policy: a head reuses its cache iff "
+                    "its query similarity exceeds gamma")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale FETCH_SIZE / WRITE_SIZE "
@@ -164,7 +173,18 @@ def main() -> int:
     log(f"[bench] workload {w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} D={w.head_dim} Lb={w.block_len} "
         f"Lp={w.prefix_len} S={w.steps} blocks={w.n_blocks} r={r}")
     t_gen = time.perf_counter()
-    prefix, blocks = wl.make_inputs(w)
+    if args.policy == "fixed":
+        prefix, blocks = wl.make_inputs(w)
+    else:   # decoding-style steps: abrupt reveals (tau) or per-head drift (gamma)
+        if args.sparse:
+            print("adaptive reuse policies run on the dense prefix", file=sys.stderr)
+            return 2
+        rng = np.random.default_rng(w.seed)
+        prefix = wl.make_prefix(w, rng)
+        blocks = [wl.make_block_steps_decoding(w, rng, 0.9 if args.policy == "gamma" else 0.0,
+                                               reveal=args.policy == "tau") for _ in range(w.n_blocks)]
+        if args.tau <= 0:
+            args.tau = max(1, w.block_len // 4)
     log(f"[bench] inputs drawn in {time.perf_counter() - t_gen:.1f} s")
 
     # per-block prefix: blocks after the first see the earlier blocks' final K/V appended
@@ -216,7 +236,12 @@ def main() -> int:
             kp, vp = layers[j][layer]
             for s in range(w.steps):
                 q, k, v = steps_dev[j][s]
-                st.step(q, k, v, kp, vp, s, rr, mode, want_lse=False)
+                if mode == "cached" and args.policy != "fixed":
+                    _, kprev, vprev = steps_dev[j][max(s - 1, 0)]
+                    st.step_policy(q, k, v, kprev, vprev, kp, vp, s, args.policy, args.tau, args.eps, args.gamma,
+                                   want_lse=False)
+                else:
+                    st.step(q, k, v, kp, vp, s, rr, mode, want_lse=False)
 
     def timed(fn, n):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,15 +266,26 @@ def main() -> int:
     st0 = states[0]
     lat = {"refresh": [], "reuse": []}
     n_rep = max(20, args.steps // 2)   # >= 20 refresh steps (one per block pass)
+    recomputed = []   # policy mode: fraction of (stream, KV head) partials recomputed per step
     for rep in range(n_rep):
         kp, vp = layers[0][rep % N_LAYERS]
         for s in range(w.steps):
             q, k, v = steps_dev[0][s]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            refreshed = st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+            if args.policy == "fixed":
+                refreshed = st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+            else:
+                _, kprev, vprev = steps_dev[0][max(s - 1, 0)]
+                st0.step_policy(q, k, v, kprev, vprev, kp, vp, s, args.policy, args.tau, args.eps, args.gamma,
+                                want_lse=False)
             e1.record()
             torch.cuda.synchronize()
+            if args.policy != "fixed":
+                frac = float(st0.mask.float().mean())
+                refreshed = frac > 0
+                if rep == 0:
+                    recomputed.append(frac)
             lat["refresh" if refreshed else "reuse"].append(e0.elapsed_time(e1) * 1e3)
     med = lambda xs: float(np.median(xs)) if xs else None
     pct = lambda xs, q: float(np.percentile(xs, q)) if xs else None
@@ -289,7 +325,12 @@ def main() -> int:
         full_o.append(st0.o.float().clone())
     for s in range(w.steps):
         q, k, v = steps_dev[0][s]
-        st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+        if args.policy == "fixed":
+            st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
+        else:
+            _, kprev, vprev = steps_dev[0][max(s - 1, 0)]
+            st0.step_policy(q, k, v, kprev, vprev, kp, vp, s, args.policy, args.tau, args.eps, args.gamma,
+                            want_lse=False)
         drift.append(float((st0.o.float() - full_o[s]).abs().max()))
 
     sparse_only_drift = None
@@ -346,7 +387,9 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) draws, bf16-rounded, block random walk)",
+        "data": ("synthetic (seeded N(0,1) draws, bf16-rounded, block random walk)" if args.policy == "fixed" else
+                 "synthetic (seeded N(0,1) draws, bf16-rounded, decoding-style block steps: "
+                 + ("uneven token reveals)" if args.policy == "tau" else "per-head drift spread 0.9)")),
         "config": {
             "workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
             "block_len": w.block_len, "prefix_len": lens if w.batch > 1 else lens[0],
@@ -355,7 +398,11 @@ def main() -> int:
             "sparse": (f"{int(st0.chunks.shape[-1])} of 64-token chunks per KV head selected; residual cached"
                        if args.sparse else None),
             "step": "one block of denoise_steps attention steps, one layer",
+            "policy": ({"name": "fixed", "refresh_period": r} if args.policy == "fixed" else
+                       {"name": args.policy, "tau": args.tau, "eps": args.eps} if args.policy == "tau" else
+                       {"name": "gamma", "gamma": args.gamma}),
         },
+        "recompute_fraction_per_step": recomputed if args.policy != "fixed" else None,
         "full_recompute": {"value": q_tokens / (ms_full * 1e-3), "unit": "query-tok/s", "ms_per_step": ms_full},
         "speedup_vs_full": ms_full / ms_cached,
         "step_latency_us": {"refresh_median": med(lat["refresh"]), "refresh_p10": pct(lat["refresh"], 10),

@@ -534,6 +534,7 @@ fb_status fb_refresh_mask_gamma(const fb_desc* d, const void* q_cur, void* q_ref
   if (gamma != gamma) return fail(FB_ERR_ARG, "gamma is NaN");
   if (!q_cur || !q_ref || !sim_out || !mask_out)
     return fail(FB_ERR_NULL, "q_cur, q_ref, sim_out and mask_out are required");
+  if (!aligned16(q_cur) || !aligned16(q_ref)) return fail(FB_ERR_ALIGN, "q_cur and q_ref must be 16-byte aligned");
   fb::GammaArgs g;
   memset(&g, 0, sizeof(g));
   g.q_cur = q_cur;

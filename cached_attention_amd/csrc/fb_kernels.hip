@@ -936,27 +936,51 @@ __global__ void __launch_bounds__(256) tau_finalize_kernel(const TauArgs t) {
 // reference step (q_ref) and now (fp64 sums, so the threshold decision does
 // not hinge on fp32 summation order); the KV head is recomputed iff some
 // similarity is <= gamma (or step 0), and then the group's q_ref rows take
-// the current queries.
-__global__ void __launch_bounds__(256) gamma_kernel(const GammaArgs a) {
-  __shared__ double red[3][4];
+// the current queries.  Rows move as 8-element (16- or 32-byte) vectors.
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, double* out) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = (double)(float)v[j];
+  } else {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[j] = a[j];
+      out[4 + j] = b[j];
+    }
+  }
+}
+
+template <typename T>
+__device__ void gamma_group(const GammaArgs& a) {
+  constexpr int NT = 1024;
+  __shared__ double red[3][NT / 64];
   const int b = blockIdx.x / a.Hkv;
   const int g = blockIdx.x % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int n = a.Lb * a.D;
+  const int cs = a.D == 128 ? 4 : 3;   // log2 of 8-element chunks per row
+  const int nv = a.Lb << cs;           // 8-element chunks per head
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const T* qc = (const T*)a.q_cur;
+  T* qr = (T*)a.q_ref;
   bool refresh = a.step == 0;
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
     double dot = 0.0, n1 = 0.0, n2 = 0.0;
-    for (int e = threadIdx.x; e < n; e += 256) {
-      const int pos = e / a.D, dd = e % a.D;
-      const double x = ld_elem(a.q_ref, (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + dd, a.dtype);
-      const double y = ld_elem(a.q_cur, (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + dd,
-                               a.dtype);
-      dot += x * y;
-      n1 += x * x;
-      n2 += y * y;
+    for (int i = threadIdx.x; i < nv; i += NT) {
+      const int pos = i >> cs, c8 = (i & ((1 << cs) - 1)) * 8;
+      double x[8], y[8];
+      ld8(qr + (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + c8, x);
+      ld8(qc + (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + c8, y);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dot = fma(x[j], y[j], dot);
+        n1 = fma(x[j], x[j], n1);
+        n2 = fma(y[j], y[j], n2);
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -970,9 +994,13 @@ __global__ void __launch_bounds__(256) gamma_kernel(const GammaArgs a) {
       red[2][wave] = n2;
     }
     __syncthreads();
-    const double sd = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const double s1 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    const double s2 = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    double sd = 0.0, s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      sd += red[0][w];
+      s1 += red[1][w];
+      s2 += red[2][w];
+    }
     const double sim = (s1 > 0.0 && s2 > 0.0) ? sd / sqrt(s1 * s2) : 0.0;
     if (threadIdx.x == 0) a.sim[(int64_t)b * a.Hq + h] = (float)sim;
     refresh |= !(sim > (double)a.gamma);
@@ -980,17 +1008,25 @@ __global__ void __launch_bounds__(256) gamma_kernel(const GammaArgs a) {
   }
   if (threadIdx.x == 0) a.mask[(int64_t)b * a.Hkv + g] = refresh ? 1 : 0;
   if (!refresh) return;
-  const int esz = a.dtype == kDtypeBf16 ? 2 : 4;
-  for (int e = threadIdx.x; e < G * n; e += 256) {
-    const int hh = e / n, r = e % n;
-    const int h = g * G + hh, pos = r / a.D, dd = r % a.D;
-    const int64_t src = (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + dd;
-    const int64_t dst = (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + dd;
-    if (esz == 2)
-      ((__bf16*)a.q_ref)[dst] = ((const __bf16*)a.q_cur)[src];
-    else
-      ((float*)a.q_ref)[dst] = ((const float*)a.q_cur)[src];
+  for (int i = threadIdx.x; i < G * nv; i += NT) {   // 16-byte moves
+    const int h = g * G + i / nv, r = i % nv;
+    const int pos = r >> cs, c8 = (r & ((1 << cs) - 1)) * 8;
+    const T* src = qc + (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh + c8;
+    T* dst = qr + (((int64_t)b * a.Lb + pos) * a.Hq + h) * a.D + c8;
+    if constexpr (sizeof(T) == 2) {
+      *(bf16x8*)dst = *(const bf16x8*)src;
+    } else {
+      *(f32x4*)dst = *(const f32x4*)src;
+      *(f32x4*)(dst + 4) = *(const f32x4*)(src + 4);
+    }
   }
+}
+
+__global__ void __launch_bounds__(1024) gamma_kernel(const GammaArgs a) {
+  if (a.dtype == kDtypeBf16)
+    gamma_group<__bf16>(a);
+  else
+    gamma_group<float>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -1061,7 +1097,7 @@ int launch_tau(const TauArgs& t, void* stream) {
 
 int launch_gamma(const GammaArgs& g, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)((int64_t)g.B * g.Hkv)), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(gamma_kernel, dim3((unsigned)((int64_t)g.B * g.Hkv)), dim3(1024), 0, s, g);
   return (int)hipGetLastError();
 }
 

@@ -50,6 +50,37 @@ class AttentionStep:
                            self.o_res, self.lse_res, self.o, self.lse if want_lse else None, step,
                            refresh_period, m, force_refresh, self.ws, self.ws_bytes, stream)
 
+    def step_policy(self, q, k, v, k_prev, v_prev, k_pre, v_pre, step: int, policy: str, tau: int = 0,
+                    eps: float = 0.0, gamma: float = 0.0, want_lse: bool = True, stream=None) -> None:
+        """One dense step under an adaptive reuse policy (dense prefix only).
+
+        "tau": recompute a stream's block-external partials iff the number of
+        block tokens whose K/V changed by more than eps since the previous step
+        (k_prev, v_prev) reaches tau.  "gamma": recompute a KV head iff one of its
+        query heads' block queries has cosine similarity <= gamma with the queries
+        its cache was computed from.  The decision stays on the device:
+        ``self.mask`` [B][Hkv] (1 = recomputed at this step), ``self.count`` [B]
+        (tau) and ``self.sim`` [B][Hq] (gamma) hold the last step's values.
+        """
+        if self.sparse is not None:
+            raise ValueError("adaptive reuse policies run on the dense prefix")
+        b_n, hq, hkv, d, lb = self.shape
+        if not hasattr(self, "mask"):
+            dev = self.o.device
+            self.mask = torch.zeros(b_n, hkv, dtype=torch.int32, device=dev)
+            self.count = torch.zeros(b_n, dtype=torch.int32, device=dev)
+            self.sim = torch.zeros(b_n, hq, dtype=torch.float32, device=dev)
+            self.q_ref = torch.zeros(b_n, lb, hq, d, dtype=self.tdtype, device=dev)
+        if policy == "tau":
+            fbl.fb_refresh_mask_tau(self.desc, k_prev, v_prev, k, v, eps, tau, step, self.count, self.mask,
+                                    self.ws, self.ws_bytes, stream)
+        elif policy == "gamma":
+            fbl.fb_refresh_mask_gamma(self.desc, q, self.q_ref, gamma, step, self.sim, self.mask, stream)
+        else:
+            raise ValueError(policy)
+        fbl.fb_step_masked(self.desc, q, k, v, k_pre, v_pre, self.mask, self.o_ext, self.lse_ext, self.o,
+                           self.lse if want_lse else None, self.ws, self.ws_bytes, stream)
+
     def prefix(self, q, k_pre, v_pre, chunk_mode: Optional[int] = None, stream=None) -> None:
         sp = None
         if chunk_mode is not None:
