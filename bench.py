@@ -22,6 +22,7 @@ fp64 oracle timed on the host cores as a baseline.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -136,6 +137,8 @@ def main() -> int:
                     "changed by more than eps")
     ap.add_argument("--gamma", type=float, default=0.99, help="gamma policy: a head reuses its cache iff "
                     "its query similarity exceeds gamma")
+    ap.add_argument("--prefix-len", type=int, default=0,
+                    help="override the workload's prefix length (tokens per stream), e.g. a 128K -> 800K sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale FETCH_SIZE / WRITE_SIZE "
@@ -168,6 +171,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
         return 0
     w = wl.WORKLOADS[args.workload]
+    if args.prefix_len > 0:
+        w = dataclasses.replace(w, name=f"{w.name}@{args.prefix_len}", prefix_len=args.prefix_len)
     r = args.r
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} D={w.head_dim} Lb={w.block_len} "

@@ -577,4 +577,35 @@ fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk,
   return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
 }
 
+fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk, void* k_pre, void* v_pre,
+                          const int64_t* dst_rows_dev, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st != FB_OK) return st;
+  if (!k_blk || !v_blk || !k_pre || !v_pre || !dst_rows_dev)
+    return fail(FB_ERR_NULL, "k_blk, v_blk, k_pre, v_pre and dst_rows_dev are required");
+  if (!aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pre) || !aligned16(v_pre))
+    return fail(FB_ERR_ALIGN, "all tensor base pointers must be 16-byte aligned");
+  if ((int64_t)d->batch * d->block_len * d->hkv * d->head_dim > (1LL << 40))
+    return fail(FB_ERR_SHAPE, "block too large");
+  fb::AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_pre = k_pre;
+  a.v_pre = v_pre;
+  a.kv_sb = d->kv_stride_b;
+  a.kv_st = d->kv_stride_t;
+  a.kv_sh = d->kv_stride_h;
+  a.pre_st = d->pre_stride_t;
+  a.pre_sh = d->pre_stride_h;
+  a.dst_rows = dst_rows_dev;
+  a.B = d->batch;
+  a.Lb = d->block_len;
+  a.Hkv = d->hkv;
+  a.D = d->head_dim;
+  a.esize = esize(d);
+  return hip_status(fb::launch_append(a, stream), "block append launch");
+}
+
 }  // extern "C"

@@ -139,6 +139,18 @@ int launch_combine(const CombineArgs& c, int64_t rows, void* stream);
 int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* la, const float* ob,
                  const float* lb, float* o, float* lse, void* stream);
 int launch_tau(const TauArgs& t, void* stream);
+// block append: copy [B][Lb][Hkv][D] rows (block strides) into prefix rows
+struct AppendArgs {
+  const void* k_blk;
+  const void* v_blk;
+  void* k_pre;
+  void* v_pre;
+  int64_t kv_sb, kv_st, kv_sh;   // block strides (elements)
+  int64_t pre_st, pre_sh;        // prefix strides (elements)
+  const int64_t* dst_rows;       // [B] device
+  int32_t B, Lb, Hkv, D, esize;
+};
+int launch_append(const AppendArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
 
 }  // namespace fb

@@ -1030,6 +1030,30 @@ __global__ void __launch_bounds__(1024) gamma_kernel(const GammaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// finalised block -> prefix KV cache: one thread per 16-byte piece of a row
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
+  const int pieces = a.D * a.esize / 16;   // 16-byte pieces per (token, KV head) row
+  const int64_t per_tensor = (int64_t)a.B * a.Lb * a.Hkv * pieces;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * per_tensor) return;
+  const bool is_v = i >= per_tensor;
+  if (is_v) i -= per_tensor;
+  const int pc = (int)(i % pieces);
+  int64_t r = i / pieces;
+  const int g = (int)(r % a.Hkv);
+  r /= a.Hkv;
+  const int t = (int)(r % a.Lb);
+  const int b = (int)(r / a.Lb);
+  const int64_t src = (int64_t)b * a.kv_sb + (int64_t)t * a.kv_st + (int64_t)g * a.kv_sh;
+  const int64_t dst = (ld_const(a.dst_rows, b) + t) * a.pre_st + (int64_t)g * a.pre_sh;
+  const char* s = (const char*)(is_v ? a.v_blk : a.k_blk) + src * a.esize + pc * 16;
+  char* d = (char*)(is_v ? a.v_pre : a.k_pre) + dst * a.esize + pc * 16;
+  *(f32x4*)d = *(const f32x4*)s;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1092,6 +1116,12 @@ int launch_tau(const TauArgs& t, void* stream) {
   const int64_t toks = (int64_t)t.B * t.Lb;
   hipLaunchKernelGGL(tau_flags_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tau_finalize_kernel, dim3((unsigned)t.B), dim3(256), 0, s, t);
+  return (int)hipGetLastError();
+}
+
+int launch_append(const AppendArgs& a, void* stream) {
+  const int64_t n = 2LL * a.B * a.Lb * a.Hkv * (a.D * a.esize / 16);
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 

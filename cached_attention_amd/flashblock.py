@@ -25,7 +25,7 @@ FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 
 EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
            "fb_block_attn", "fb_merge", "fb_step", "fb_refresh_mask_tau", "fb_refresh_mask_gamma",
-           "fb_step_masked", "fb_status_string", "fb_last_error", "fb_abi_version")
+           "fb_step_masked", "fb_append_block", "fb_status_string", "fb_last_error", "fb_abi_version")
 
 
 class FlashBlockError(RuntimeError):
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         l.fb_refresh_mask_gamma.restype = i32
         l.fb_step_masked.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         l.fb_step_masked.restype = i32
+        l.fb_append_block.argtypes = [D, P, P, P, P, P, P]
+        l.fb_append_block.restype = i32
         l.fb_status_string.argtypes = [i32]
         l.fb_status_string.restype = ctypes.c_char_p
         l.fb_last_error.argtypes = []
@@ -238,6 +240,11 @@ def fb_step_masked(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, mask, o_ext_ca
     _check(lib().fb_step_masked(desc.ref, _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre),
                                 _ptr(mask), _ptr(o_ext_cache), _ptr(lse_ext_cache), _ptr(o), _ptr(lse_out),
                                 _ptr(ws), ws_bytes, _stream(stream)), "fb_step_masked")
+
+
+def fb_append_block(desc: Desc, k_blk, v_blk, k_pre, v_pre, dst_rows_dev, stream=None) -> None:
+    _check(lib().fb_append_block(desc.ref, _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre), _ptr(dst_rows_dev),
+                                 _stream(stream)), "fb_append_block")
 
 
 def fb_status_string(status: int) -> str:

@@ -210,6 +210,17 @@ fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk,
                          const void* k_pre, const void* v_pre, const int32_t* mask, float* o_ext_cache,
                          float* lse_ext_cache, void* o, float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Append the finalised block to the prefix KV cache (the cache the next
+ * blocks read as J_out grows by each finalised block; explainer page, Problem
+ * Statement).  Copies stream b's block K/V rows [Lb][Hkv][D] (fb_desc block
+ * strides) into prefix rows dst_rows_dev[b] .. dst_rows_dev[b] + Lb - 1 of
+ * k_pre / v_pre (fb_desc prefix strides, i.e. row r of KV head g at
+ * r * pre_stride_t + g * pre_stride_h).  dst_rows_dev is int64 [B] in device
+ * memory; the caller owns the capacity and afterwards describes the grown
+ * prefix with new offsets.  Rows outside the written ones are not touched. */
+fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk, void* k_pre, void* v_pre,
+                          const int64_t* dst_rows_dev, void* stream);
+
 const char* fb_status_string(fb_status s);
 const char* fb_last_error(void);
 int32_t fb_abi_version(void);

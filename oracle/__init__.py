@@ -40,6 +40,7 @@ from .attention import (  # noqa: F401
     to_output_layout,
     sparse_only_step,
     grow_prefix,
+    append_block_rows,
     BlockResult,
 )
 from .policies import (  # noqa: F401

@@ -289,3 +289,23 @@ def grow_prefix(k_pre, v_pre, offsets, k_last, v_last):
         vs.append(v_last[b])
         new_off[b + 1] = new_off[b] + (t1 - t0) + k_last.shape[1]
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0), new_off
+
+
+def append_block_rows(k_pre, v_pre, k_last, v_last, dst_rows):
+    """Write each stream's finalised block K/V into given prefix rows.
+
+    Once a block is final it joins the growing KV cache that the next blocks'
+    queries read as J_out (explainer page, Problem Statement: block-wise
+    causal inference over a growing KV cache).  Stream b's Lb rows go to
+    prefix rows dst_rows[b] ..
+    dst_rows[b] + Lb - 1 (all KV heads).  Returns new arrays; the inputs are
+    not modified.
+    """
+    k_new = np.array(k_pre, copy=True)
+    v_new = np.array(v_pre, copy=True)
+    lb = k_last.shape[1]
+    for b in range(k_last.shape[0]):
+        r0 = int(dst_rows[b])
+        k_new[r0:r0 + lb] = k_last[b]
+        v_new[r0:r0 + lb] = v_last[b]
+    return k_new, v_new

@@ -150,3 +150,11 @@ def test_adaptive_reuse_validation():
     assert sm(mask=None) == fbl.FB_ERR_NULL
     assert sm(q=FAKE + 2) == fbl.FB_ERR_ALIGN
     assert sm(wsb=ws_b - 1) == fbl.FB_ERR_WORKSPACE
+
+
+def test_append_block_validation():
+    d = _desc()
+    lib = fbl.lib()
+    assert lib.fb_append_block(d.ref, FAKE, FAKE, FAKE, FAKE, None, None) == fbl.FB_ERR_NULL
+    assert lib.fb_append_block(d.ref, FAKE, FAKE + 8, FAKE, FAKE, FAKE, None) == fbl.FB_ERR_ALIGN
+    assert lib.fb_append_block(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == fbl.FB_ERR_NULL

@@ -523,3 +523,24 @@ def test_tau_policy_counts_follow_reveals():
     for s in range(1, w.steps):
         assert got.counts[s].tolist() == [counts[s - 1]] * 2
         assert got.masks[s].tolist() == [[int(counts[s - 1] >= 3)] * 2] * 2
+
+
+def test_append_block_rows_at_stream_ends_equals_grow_prefix():
+    """Writing each stream's block at the end of its region of a buffer laid out
+    for the grown offsets reproduces the concatenation of grow_prefix."""
+    rng = np.random.default_rng(15)
+    offsets = np.array([0, 5, 12], dtype=np.int64)
+    k_pre, v_pre = _rand(rng, 12, 2, 4), _rand(rng, 12, 2, 4)
+    kl, vl = _rand(rng, 2, 3, 2, 4), _rand(rng, 2, 3, 2, 4)
+    k2, v2, off2 = oracle.grow_prefix(k_pre, v_pre, offsets, kl, vl)
+    kb = np.zeros_like(k2)
+    vb = np.zeros_like(v2)
+    for b in range(2):   # old rows into the grown layout, then the block at each stream's end
+        n = int(offsets[b + 1] - offsets[b])
+        kb[off2[b]:off2[b] + n] = k_pre[offsets[b]:offsets[b + 1]]
+        vb[off2[b]:off2[b] + n] = v_pre[offsets[b]:offsets[b + 1]]
+    dst = [int(off2[b] + offsets[b + 1] - offsets[b]) for b in range(2)]
+    k3, v3 = oracle.append_block_rows(kb, vb, kl, vl, dst)
+    np.testing.assert_array_equal(k3, k2)
+    np.testing.assert_array_equal(v3, v2)
+    assert not np.array_equal(kb, k3)   # inputs untouched

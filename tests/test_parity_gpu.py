@@ -318,3 +318,50 @@ def test_full_size_video():
     w = wl.WORKLOADS["video_1560"]
     prefix, blocks = wl.make_inputs(wl.ci_version(w, prefix_len=w.prefix_len, n_blocks=1))
     _sampled_check(w, prefix, blocks[0], heads=[(0, 0), (0, 11)])
+
+
+@pytest.mark.parametrize("layout", ["token", "head"])
+def test_append_block_grows_prefix_exactly(layout):
+    """The finalised block's K/V land in the grown prefix bit for bit (oracle
+    grow_prefix), and the next block's step over that prefix matches the oracle."""
+    w = wl.Workload("grow", "bf16", 2, 8, 2, 128, 24, 200, 3, 1.0, 0.1, ragged=0.25, seed=61)
+    rng = np.random.default_rng(61)
+    prefix = wl.make_prefix(w, rng)
+    blk0, blk1 = wl.make_block_steps(w, rng), wl.make_block_steps(w, rng)
+    k_last, v_last = blk0.k[-1], blk0.v[-1]
+    k2, v2, off2 = oracle.grow_prefix(prefix.k, prefix.v, prefix.offsets, k_last, v_last)
+    t2 = int(off2[-1])
+    lens = [int(prefix.offsets[b + 1] - prefix.offsets[b]) for b in range(w.batch)]
+    bf = torch.bfloat16
+    # the grown buffer: old rows moved to the new layout on the device, then the append
+    kd = torch.zeros(t2, w.hkv, w.head_dim, dtype=bf, device="cuda")
+    vd = torch.zeros_like(kd)
+    kp_old, vp_old = dev(prefix.k, bf), dev(prefix.v, bf)
+    for b in range(w.batch):
+        o0, o1 = int(prefix.offsets[b]), int(prefix.offsets[b + 1])
+        kd[int(off2[b]):int(off2[b]) + lens[b]] = kp_old[o0:o1]
+        vd[int(off2[b]):int(off2[b]) + lens[b]] = vp_old[o0:o1]
+    if layout == "head":   # [Hkv][T][D]
+        kd = kd.permute(1, 0, 2).contiguous()
+        vd = vd.permute(1, 0, 2).contiguous()
+        pre_strides = (w.head_dim, t2 * w.head_dim)
+    else:
+        pre_strides = None
+    off_dev = torch.tensor(off2, dtype=torch.int64, device="cuda")
+    desc = fbl.Desc(fbl.FB_BF16, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, off2, off_dev,
+                    pre_strides=pre_strides)
+    dst = torch.tensor([int(off2[b]) + lens[b] for b in range(w.batch)], dtype=torch.int64, device="cuda")
+    fbl.fb_append_block(desc, dev(k_last, bf), dev(v_last, bf), kd, vd, dst)
+    torch.cuda.synchronize()
+    kg, vg = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    if layout == "head":
+        kg, vg = kg.transpose(1, 0, 2), vg.transpose(1, 0, 2)
+    np.testing.assert_array_equal(kg, k2)
+    np.testing.assert_array_equal(vg, v2)
+    # the next block over the grown prefix
+    grown = wl.Prefix(k2, v2, off2)
+    st = AttentionStep("bf16", w.batch, w.hq, w.hkv, w.head_dim, w.block_len, off2, pre_strides=pre_strides)
+    ref = oracle.run_block(k2, v2, off2, blk1.q, blk1.k, blk1.v, scale_of(w), r=2)
+    got = run_gpu(w, grown, blk1, r=2, st=st, k_pre=kd, v_pre=vd)
+    for s in range(w.steps):
+        assert np.abs(got.out[s] - ref.out[s]).max() <= 2e-2
