@@ -49,4 +49,7 @@ from .policies import (  # noqa: F401
     head_similarity,
     gamma_mask,
     run_block_policy,
+    pooled_chunk_keys,
+    chunk_scores,
+    select_chunks,
 )

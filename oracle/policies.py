@@ -141,3 +141,61 @@ def run_block_policy(k_pre, v_pre, offsets, q_steps, k_steps, v_steps, scale: fl
         res.lse_ext.append(cache_l.copy())
         res.masks.append(mask)
     return res
+
+
+# ---------------------------------------------------------------------------
+# Chunk selection for the sparse variant
+# ---------------------------------------------------------------------------
+#
+# The pages combine FlashBlock with a sparse-attention selector (SparseD at
+# 20-40% density; "Compatibility with Sparse Attention") without stating the
+# selector.  Reading taken here (the plainest block-level rule): a chunk of
+# chunk_len prefix tokens is represented by the mean of its keys; its score
+# for a (stream, KV head) is the largest dot product any query of the KV
+# head's group has with that pooled key; the k best chunks are kept, ties
+# going to the lower chunk index, listed ascending.
+
+def pooled_chunk_keys(k_pre, offsets, chunk_len: int = 64):
+    """Mean key per chunk: list over streams of [n_chunks_b][Hkv][D] (fp64)."""
+    out = []
+    for b in range(len(offsets) - 1):
+        t0, t1 = int(offsets[b]), int(offsets[b + 1])
+        n = -(-(t1 - t0) // chunk_len)
+        pk = np.zeros((n, k_pre.shape[1], k_pre.shape[2]))
+        for c in range(n):
+            a, z = t0 + c * chunk_len, min(t0 + (c + 1) * chunk_len, t1)
+            pk[c] = np.asarray(k_pre[a:z], np.float64).mean(axis=0)
+        out.append(pk)
+    return out
+
+
+def chunk_scores(q_blk, pooled):
+    """score[b][g][c] = max over the group's block queries of q . pooled key."""
+    b_n, lb, hq, d = q_blk.shape
+    hkv = pooled[0].shape[1] if len(pooled[0]) else 1
+    scores = []
+    for b in range(b_n):
+        n = pooled[b].shape[0]
+        sb = np.full((hkv, n), -np.inf)
+        for g in range(hkv):
+            qs = np.concatenate([np.asarray(q_blk[b, :, h, :], np.float64)
+                                 for h in range(hq) if kv_group(h, hq, hkv) == g], axis=0)
+            if n:
+                sb[g] = (qs @ pooled[b][:, g, :].T).max(axis=0)
+        scores.append(sb)
+    return scores
+
+
+def select_chunks(q_blk, k_pre, offsets, k: int, chunk_len: int = 64):
+    """Top-k chunk indices per (stream, KV head), ascending: int32 [B][Hkv][k]."""
+    pooled = pooled_chunk_keys(k_pre, offsets, chunk_len)
+    scores = chunk_scores(q_blk, pooled)
+    b_n = len(scores)
+    hkv = scores[0].shape[0]
+    idx = np.zeros((b_n, hkv, k), dtype=np.int32)
+    for b in range(b_n):
+        for g in range(hkv):
+            s = scores[b][g]
+            order = sorted(range(len(s)), key=lambda c: (-s[c], c))   # best first, ties: lower index
+            idx[b, g] = np.sort(np.array(order[:k], dtype=np.int32))
+    return idx

@@ -544,3 +544,41 @@ def test_append_block_rows_at_stream_ends_equals_grow_prefix():
     np.testing.assert_array_equal(k3, k2)
     np.testing.assert_array_equal(v3, v2)
     assert not np.array_equal(kb, k3)   # inputs untouched
+
+
+def test_chunk_selection_constructed():
+    """Pooled keys are chunk means (the last chunk over its own tokens); scores
+    are the max over the KV group's queries; top-k keeps the best, ties to the
+    lower index, ascending."""
+    hkv, d, cl = 2, 4, 4
+    offsets = np.array([0, 10], dtype=np.int64)   # chunks of 4, 4, 2 tokens
+    k_pre = np.zeros((10, hkv, d))
+    k_pre[0:4, 0, 0] = [1, 2, 3, 6]               # chunk 0, head 0: mean e0 * 3
+    k_pre[4:8, 0, 1] = 2.0                        # chunk 1, head 0: mean e1 * 2
+    k_pre[8:10, 0, 0] = [-1, -3]                  # chunk 2, head 0: mean e0 * -2
+    k_pre[8:10, 1, 2] = 5.0                       # chunk 2, head 1: mean e2 * 5
+    pooled = oracle.pooled_chunk_keys(k_pre, offsets, cl)
+    np.testing.assert_allclose(pooled[0][0, 0], [3, 0, 0, 0])
+    np.testing.assert_allclose(pooled[0][2, 0], [-2, 0, 0, 0])
+    q = np.zeros((1, 2, 4, d))                    # hq 4 -> heads {0,1} on KV 0, {2,3} on KV 1
+    q[0, 0, 1, :] = [1, 0, 0, 0]                  # a KV-0 query along e0
+    q[0, 1, 0, :] = [0, 2, 0, 0]                  # another along e1
+    q[0, 0, 3, :] = [0, 0, 1, 0]                  # a KV-1 query along e2
+    sc = oracle.chunk_scores(q, pooled)[0]
+    np.testing.assert_allclose(sc[0], [3.0, 4.0, 0.0])   # max over the group's queries and positions
+    np.testing.assert_allclose(sc[1], [0.0, 0.0, 5.0])
+    sel = oracle.select_chunks(q, k_pre, offsets, 2, cl)
+    assert sel[0, 0].tolist() == [0, 1]           # 4.0 and 3.0
+    assert sel[0, 1].tolist() == [0, 2]           # 5.0, then a tie at 0.0: lower index 0
+    # a brute-force check on random data: the kept set has the k largest scores
+    rng = np.random.default_rng(16)
+    offsets = np.array([0, 300, 700], dtype=np.int64)
+    kp = _rand(rng, 700, hkv, d)
+    qq = _rand(rng, 2, 3, 4, d)
+    sel = oracle.select_chunks(qq, kp, offsets, 3, 64)
+    scs = oracle.chunk_scores(qq, oracle.pooled_chunk_keys(kp, offsets, 64))
+    for b in range(2):
+        for g in range(hkv):
+            kept = set(sel[b, g].tolist())
+            assert len(kept) == 3 and sorted(kept) == sel[b, g].tolist()
+            assert min(scs[b][g][list(kept)]) >= max(np.delete(scs[b][g], list(kept)))
