@@ -608,4 +608,70 @@ fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk
   return hip_status(fb::launch_append(a, stream), "block append launch");
 }
 
+size_t fb_select_chunks_ws(const fb_desc* d, int32_t chunk_len) {
+  clear_error();
+  if (check_desc(d) != FB_OK || check_offsets(d) != FB_OK) return 0;
+  if (chunk_len < 1) {
+    fail(FB_ERR_ARG, "chunk_len = %d < 1", chunk_len);
+    return 0;
+  }
+  int64_t total = 0;
+  for (int b = 0; b < d->batch; ++b)
+    total += ceil_div(d->prefix_offsets_host[b + 1] - d->prefix_offsets_host[b], chunk_len);
+  const size_t pooled = align_up((size_t)total * d->hkv * d->head_dim * sizeof(float));
+  const size_t scores = align_up((size_t)total * d->hkv * sizeof(float));
+  return std::max<size_t>(pooled + scores, kAlign);
+}
+
+fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pre, int32_t chunk_len, int32_t k,
+                           int32_t* chunk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st != FB_OK) return st;
+  if (chunk_len < 1) return fail(FB_ERR_ARG, "chunk_len = %d < 1", chunk_len);
+  if (k < 1) return fail(FB_ERR_ARG, "k = %d < 1", k);
+  if (!q_blk || !k_pre || !chunk_idx_out) return fail(FB_ERR_NULL, "q_blk, k_pre and chunk_idx_out are required");
+  if (!aligned16(q_blk) || !aligned16(k_pre)) return fail(FB_ERR_ALIGN, "q_blk and k_pre must be 16-byte aligned");
+  int64_t total = 0, tiles = 0;
+  for (int b = 0; b < d->batch; ++b) {
+    const int64_t n = ceil_div(d->prefix_offsets_host[b + 1] - d->prefix_offsets_host[b], chunk_len);
+    if (n < k) return fail(FB_ERR_ARG, "stream %d has %lld chunks < k = %d", b, (long long)n, k);
+    if (n > fb::kMaxSelectChunks)
+      return fail(FB_ERR_SHAPE, "stream %d has %lld chunks > %d", b, (long long)n, fb::kMaxSelectChunks);
+    total += n;
+    tiles += (int64_t)d->hkv * ceil_div(n, 64);
+  }
+  if (total * d->hkv > (1LL << 30) || tiles > (1LL << 30)) return fail(FB_ERR_SHAPE, "prefix too large");
+  const size_t pooled = align_up((size_t)total * d->hkv * d->head_dim * sizeof(float));
+  const size_t need = fb_select_chunks_ws(d, chunk_len);
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+  fb::SelectArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q_blk;
+  a.q_sb = d->q_stride_b;
+  a.q_st = d->q_stride_t;
+  a.q_sh = d->q_stride_h;
+  a.k_pre = k_pre;
+  a.pre_st = d->pre_stride_t;
+  a.pre_sh = d->pre_stride_h;
+  a.offsets = d->prefix_offsets_dev;
+  a.B = d->batch;
+  a.Hq = d->hq;
+  a.Hkv = d->hkv;
+  a.G = d->hq / d->hkv;
+  a.Lb = d->block_len;
+  a.D = d->head_dim;
+  a.dtype = d->dtype;
+  a.chunk_len = chunk_len;
+  a.k = k;
+  a.total_chunks = (int32_t)total;
+  a.work_tiles = (int32_t)tiles;
+  a.pooled = (float*)ws;
+  a.scores = (float*)((char*)ws + pooled);
+  a.idx_out = chunk_idx_out;
+  return hip_status(fb::launch_select(a, stream), "chunk selection launch");
+}
+
 }  // extern "C"

@@ -151,6 +151,22 @@ struct AppendArgs {
   int32_t B, Lb, Hkv, D, esize;
 };
 int launch_append(const AppendArgs& a, void* stream);
+// chunk selection for the sparse variant: pooled chunk keys, max query score, top-k
+constexpr int kMaxSelectChunks = 16384;   // chunks per stream the top-k pass sorts in LDS
+struct SelectArgs {
+  const void* q;
+  int64_t q_sb, q_st, q_sh;
+  const void* k_pre;
+  int64_t pre_st, pre_sh;
+  const int64_t* offsets;   // device [B+1]
+  int32_t B, Hq, Hkv, G, Lb, D, dtype, chunk_len, k;
+  int32_t total_chunks;     // sum over streams of ceil(Lp_b / chunk_len)
+  int32_t work_tiles;       // sum over streams of Hkv * ceil(n_b / 64)
+  float* pooled;            // [total_chunks][Hkv][D]
+  float* scores;            // [total_chunks][Hkv]
+  int32_t* idx_out;         // [B][Hkv][k]
+};
+int launch_select(const SelectArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
 
 }  // namespace fb

@@ -1054,6 +1054,163 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// chunk selection for the sparse variant (pooled key, max query score, top-k)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int chunks_of(const int64_t* off, int b, int cl) {
+  return (int)((prefix_len(off, b) + cl - 1) / cl);
+}
+
+// one wave per (chunk, KV head): the mean of the chunk's keys (fp32 sums)
+__global__ void __launch_bounds__(256) pool_kernel(const SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (int64_t)a.total_chunks * a.Hkv) return;
+  const int gc = (int)(w / a.Hkv), g = (int)(w % a.Hkv);
+  int b = 0, acc = 0;
+  for (; b < a.B; ++b) {
+    const int n = chunks_of(a.offsets, b, a.chunk_len);
+    if (gc < acc + n) break;
+    acc += n;
+  }
+  const int64_t s0 = ld_const(a.offsets, b);
+  const int64_t t0 = s0 + (int64_t)(gc - acc) * a.chunk_len;
+  const int64_t t1 = min(t0 + a.chunk_len, ld_const(a.offsets, b + 1));
+  const float inv = 1.f / (float)(t1 - t0);
+  for (int d = lane; d < a.D; d += 64) {
+    float sum = 0.f;
+    for (int64_t t = t0; t < t1; ++t) sum += ld_elem(a.k_pre, t * a.pre_st + (int64_t)g * a.pre_sh + d, a.dtype);
+    a.pooled[((int64_t)gc * a.Hkv + g) * a.D + d] = sum * inv;
+  }
+}
+
+// one workgroup per (stream, KV head, 64 chunks); four threads per chunk
+// split the group's query rows, then the max over them
+template <int D>
+__device__ void score_tile(const SelectArgs& a) {
+  int w = blockIdx.x, b = 0, base = 0;
+  for (; b < a.B; ++b) {
+    const int n = chunks_of(a.offsets, b, a.chunk_len);
+    const int tiles = a.Hkv * ((n + 63) / 64);
+    if (w < tiles) break;
+    w -= tiles;
+    base += n;
+  }
+  const int n = chunks_of(a.offsets, b, a.chunk_len);
+  const int per_g = (n + 63) / 64;
+  const int g = w / per_g, tile = w % per_g;
+  const int c = tile * 64 + (threadIdx.x >> 2), sub = threadIdx.x & 3;
+  float kk[D];
+  const bool live = c < n;
+  const float* pk = a.pooled + ((int64_t)(base + (live ? c : 0)) * a.Hkv + g) * D;
+#pragma unroll
+  for (int d = 0; d < D; d += 4) {
+    const f32x4 v = *(const f32x4*)(pk + d);
+    kk[d] = v[0]; kk[d + 1] = v[1]; kk[d + 2] = v[2]; kk[d + 3] = v[3];
+  }
+  float best = kNegInf;
+  const int rows = a.G * a.Lb;
+  for (int r = sub; r < rows; r += 4) {
+    const int h = g * a.G + r / a.Lb, pos = r % a.Lb;
+    const int64_t qo = (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh;
+    float dot = 0.f;
+    if (a.dtype == kDtypeBf16) {
+      const __bf16* qp = (const __bf16*)a.q + qo;
+#pragma unroll
+      for (int d = 0; d < D; d += 8) {
+        const bf16x8 qv = *(const bf16x8*)(qp + d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot = __builtin_fmaf((float)qv[j], kk[d + j], dot);
+      }
+    } else {
+      const float* qp = (const float*)a.q + qo;
+#pragma unroll
+      for (int d = 0; d < D; d += 4) {
+        const f32x4 qv = *(const f32x4*)(qp + d);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dot = __builtin_fmaf(qv[j], kk[d + j], dot);
+      }
+    }
+    best = fmaxf(best, dot);
+  }
+  best = fmaxf(best, __shfl_xor(best, 1, 64));
+  best = fmaxf(best, __shfl_xor(best, 2, 64));
+  if (live && sub == 0) a.scores[(int64_t)(base + c) * a.Hkv + g] = best;
+}
+
+__global__ void __launch_bounds__(256) score_kernel(const SelectArgs a) {
+  if (a.D == 128)
+    score_tile<128>(a);
+  else
+    score_tile<64>(a);
+}
+
+// sortable key: ascending order = descending score, then ascending chunk
+__device__ __forceinline__ uint64_t topk_key(float s, int i) {
+  uint32_t u = __builtin_bit_cast(uint32_t, s);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)(~asc) << 32) | (uint32_t)i;
+}
+
+// one workgroup per (stream, KV head): bitonic sort of the chunk keys in
+// LDS, flag the first k, write the flagged chunk indices in ascending order
+__global__ void __launch_bounds__(1024) topk_kernel(const SelectArgs a) {
+  __shared__ uint64_t keys[kMaxSelectChunks];
+  __shared__ unsigned char flag[kMaxSelectChunks];
+  __shared__ int wsum[16];
+  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int bb = 0; bb < b; ++bb) base += chunks_of(a.offsets, bb, a.chunk_len);
+  const int n = chunks_of(a.offsets, b, a.chunk_len);
+  int P = 2;
+  while (P < n) P <<= 1;
+  for (int i = tid; i < P; i += 1024) {
+    keys[i] = i < n ? topk_key(a.scores[(int64_t)(base + i) * a.Hkv + g], i) : ~0ull;
+    if (i < n) flag[i] = 0;
+  }
+  __syncthreads();
+  for (int k2 = 2; k2 <= P; k2 <<= 1) {
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = keys[i], y = keys[ixj];
+          const bool up = (i & k2) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = tid; j < a.k; j += 1024) flag[(uint32_t)keys[j]] = 1;
+  __syncthreads();
+  // compaction in index order: each thread owns a contiguous run of chunks
+  const int per = (n + 1023) / 1024;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += flag[i];
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
+  int pos = before + incl - cnt;
+  int32_t* out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.k;
+  for (int i = i0; i < i1; ++i)
+    if (flag[i]) out[pos++] = i;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1122,6 +1279,15 @@ int launch_tau(const TauArgs& t, void* stream) {
 int launch_append(const AppendArgs& a, void* stream) {
   const int64_t n = 2LL * a.B * a.Lb * a.Hkv * (a.D * a.esize / 16);
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_select(const SelectArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t waves = (int64_t)a.total_chunks * a.Hkv;
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(score_kernel, dim3((unsigned)a.work_tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((int64_t)a.B * a.Hkv)), dim3(1024), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 
 EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
            "fb_block_attn", "fb_merge", "fb_step", "fb_refresh_mask_tau", "fb_refresh_mask_gamma",
-           "fb_step_masked", "fb_append_block", "fb_status_string", "fb_last_error", "fb_abi_version")
+           "fb_step_masked", "fb_append_block", "fb_select_chunks_ws", "fb_select_chunks",
+           "fb_status_string", "fb_last_error", "fb_abi_version")
 
 
 class FlashBlockError(RuntimeError):
@@ -97,6 +98,10 @@ def lib() -> ctypes.CDLL:
         l.fb_step_masked.restype = i32
         l.fb_append_block.argtypes = [D, P, P, P, P, P, P]
         l.fb_append_block.restype = i32
+        l.fb_select_chunks_ws.argtypes = [D, i32]
+        l.fb_select_chunks_ws.restype = sz
+        l.fb_select_chunks.argtypes = [D, P, P, i32, i32, P, P, sz, P]
+        l.fb_select_chunks.restype = i32
         l.fb_status_string.argtypes = [i32]
         l.fb_status_string.restype = ctypes.c_char_p
         l.fb_last_error.argtypes = []
@@ -245,6 +250,19 @@ def fb_step_masked(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, mask, o_ext_ca
 def fb_append_block(desc: Desc, k_blk, v_blk, k_pre, v_pre, dst_rows_dev, stream=None) -> None:
     _check(lib().fb_append_block(desc.ref, _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre), _ptr(dst_rows_dev),
                                  _stream(stream)), "fb_append_block")
+
+
+def fb_select_chunks_ws(desc: Desc, chunk_len: int = 64) -> int:
+    n = lib().fb_select_chunks_ws(desc.ref, chunk_len)
+    if n == 0:
+        raise FlashBlockError(FB_ERR_ARG, "fb_select_chunks_ws", lib().fb_last_error().decode())
+    return n
+
+
+def fb_select_chunks(desc: Desc, q_blk, k_pre, chunk_len: int, k: int, chunk_idx_out, ws, ws_bytes: int,
+                     stream=None) -> None:
+    _check(lib().fb_select_chunks(desc.ref, _ptr(q_blk), _ptr(k_pre), chunk_len, k, _ptr(chunk_idx_out), _ptr(ws),
+                                  ws_bytes, _stream(stream)), "fb_select_chunks")
 
 
 def fb_status_string(status: int) -> str:

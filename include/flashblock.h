@@ -221,6 +221,21 @@ fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk,
 fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk, void* k_pre, void* v_pre,
                           const int64_t* dst_rows_dev, void* stream);
 
+/* Chunk selection for the sparse variant, on the device.  The pages pair
+ * FlashBlock with a sparse-attention selector ("Compatibility with Sparse
+ * Attention"; SparseD at 20-40% density) without stating the selector; this
+ * one is the plainest block-level rule: each chunk of chunk_len prefix tokens
+ * is represented by the mean of its keys (fp32), scored for a (stream, KV
+ * head) by the largest dot product of that KV head's block queries with it,
+ * and the k best chunks are kept (ties to the lower chunk index).  Writes
+ * chunk_idx_out [B][Hkv][k] int32, ascending per (stream, KV head) -- the
+ * fb_sparse chunk list.  Every stream needs at least k and at most 16384
+ * chunks.  ws: fb_select_chunks_ws(d, chunk_len) bytes, 256-byte aligned
+ * (pooled keys [chunks][Hkv][D] fp32, then scores [chunks][Hkv] fp32). */
+size_t fb_select_chunks_ws(const fb_desc* d, int32_t chunk_len);
+fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pre, int32_t chunk_len, int32_t k,
+                           int32_t* chunk_idx_out, void* ws, size_t ws_bytes, void* stream);
+
 const char* fb_status_string(fb_status s);
 const char* fb_last_error(void);
 int32_t fb_abi_version(void);

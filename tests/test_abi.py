@@ -158,3 +158,24 @@ def test_append_block_validation():
     assert lib.fb_append_block(d.ref, FAKE, FAKE, FAKE, FAKE, None, None) == fbl.FB_ERR_NULL
     assert lib.fb_append_block(d.ref, FAKE, FAKE + 8, FAKE, FAKE, FAKE, None) == fbl.FB_ERR_ALIGN
     assert lib.fb_append_block(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == fbl.FB_ERR_NULL
+
+
+def test_select_chunks_validation():
+    d = _desc()   # one stream of 131072 tokens: 2048 chunks of 64
+    lib = fbl.lib()
+    wsb = fbl.fb_select_chunks_ws(d, 64)
+    assert wsb == 2048 * 8 * 128 * 4 + 2048 * 8 * 4    # pooled keys + scores, both 256-aligned here
+    sel = lambda **kw: lib.fb_select_chunks(
+        kw.get("d", d.ref), kw.get("q", FAKE), FAKE, kw.get("cl", 64), kw.get("k", 205), kw.get("idx", FAKE),
+        kw.get("ws", FAKE), kw.get("wsb", wsb), None)
+    assert sel(d=None) == fbl.FB_ERR_NULL
+    assert sel(cl=0) == fbl.FB_ERR_ARG
+    assert sel(k=0) == fbl.FB_ERR_ARG
+    assert sel(k=2049) == fbl.FB_ERR_ARG             # more chunks asked for than the stream has
+    assert sel(idx=None) == fbl.FB_ERR_NULL
+    assert sel(q=FAKE + 2) == fbl.FB_ERR_ALIGN
+    assert sel(wsb=wsb - 1) == fbl.FB_ERR_WORKSPACE
+    assert sel(cl=4) == fbl.FB_ERR_SHAPE              # 32768 chunks: beyond the in-LDS top-k
+    assert lib.fb_select_chunks_ws(d.ref, 0) == 0 and fbl.fb_last_error() != ""
+    with pytest.raises(fbl.FlashBlockError):
+        fbl.fb_select_chunks_ws(d, 0)
