@@ -128,6 +128,9 @@ def main() -> int:
     ap.add_argument("--sparse", action="store_true",
                     help="chunk-sparse variant: cached residual of the unselected 64-token chunks plus a fresh "
                          "partial over the selected ones (workloads with a sparse keep fraction)")
+    ap.add_argument("--chunk-select", choices=("topk", "random"), default="topk",
+                    help="sparse variant: chunks chosen on the GPU from each block's first-step queries "
+                         "(pooled chunk keys, max query score, top-k), or a fixed seeded random stand-in")
     ap.add_argument("--policy", choices=("fixed", "tau", "gamma"), default="fixed",
                     help="refresh policy: fixed period r, or adaptive reuse on decoding-style block steps "
                          "(tau: updated-token threshold; gamma: per-head query similarity)")
@@ -230,6 +233,28 @@ def main() -> int:
     states = [AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, block_prefix[j][2],
                             pre_strides=pre_strides[j], chunks=chunks)
               for j in range(len(blocks))]
+    topk = args.sparse and args.chunk_select == "topk"
+    k_sel = int(chunks.shape[-1]) if args.sparse else 0
+    if topk:
+        # pooled chunk keys are per-layer state like the KV cache: full chunks of
+        # the append-only prefix never change, so a block pools only the chunks
+        # from the first one its predecessor's append touched (block 0: the
+        # steady state after the previous block's append)
+        blk_lens = [[int(o[b + 1] - o[b]) for b in range(w.batch)] for (_, _, o) in block_prefix]
+        cap = max(-(-l // 64) for l in blk_lens[-1])
+        first = [max(0, min(blk_lens[0]) - w.block_len) // 64] + [min(blk_lens[j - 1]) // 64
+                                                                   for j in range(1, len(blocks))]
+        pooled = [torch.empty(w.batch, cap, w.hkv, w.head_dim, device="cuda") for _ in range(N_LAYERS)]
+        scores_buf = torch.empty(w.batch, w.hkv, cap, device="cuda")
+        for layer in range(N_LAYERS):
+            fbl.fb_pool_chunk_keys(states[0].desc, layers[0][layer][0], 64, cap, 0, pooled[layer])
+        sel_ws = torch.empty(fbl.fb_select_chunks_ws(states[0].desc, 64), dtype=torch.uint8, device="cuda")
+
+    def select(j, q, layer):
+        """Top-k chunks of block j from its first-step queries, into the state's chunk list."""
+        fbl.fb_pool_chunk_keys(states[j].desc, layers[j][layer][0], 64, cap, first[j], pooled[layer])
+        fbl.fb_select_chunks_pooled(states[j].desc, q, pooled[layer], 64, cap, k_sel, scores_buf, states[j].chunks)
+
     torch.cuda.synchronize()
 
     counter = [0]
@@ -241,6 +266,8 @@ def main() -> int:
             kp, vp = layers[j][layer]
             for s in range(w.steps):
                 q, k, v = steps_dev[j][s]
+                if topk and s == 0:
+                    select(j, q, layer)
                 if mode == "cached" and args.policy != "fixed":
                     _, kprev, vprev = steps_dev[j][max(s - 1, 0)]
                     st.step_policy(q, k, v, kprev, vprev, kp, vp, s, args.policy, args.tau, args.eps, args.gamma,
@@ -278,6 +305,8 @@ def main() -> int:
             q, k, v = steps_dev[0][s]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
+            if topk and s == 0:
+                select(0, q, rep % N_LAYERS)
             if args.policy == "fixed":
                 refreshed = st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
             else:
@@ -316,6 +345,17 @@ def main() -> int:
                                                      st0.ws, st0.ws_bytes), n_k)
     qb, kb, vb = steps_dev[0][1]
     ms_block = timed(lambda: fbl.fb_block_attn(st0.desc, qb, kb, vb, st0.o_ext, st0.lse_ext, st0.o), n_k)
+    ms_select = ms_select_full = None
+    if topk:
+        sel_rot = [0]
+
+        def select_rot():
+            select(0, q0, sel_rot[0] % N_LAYERS)
+            sel_rot[0] += 1
+
+        ms_select = timed(select_rot, n_k)
+        ms_select_full = timed(lambda: fbl.fb_select_chunks(st0.desc, q0, layers[0][0][0], 64, k_sel, st0.chunks,
+                                                            sel_ws, sel_ws.numel()), n_k)
     tiny = torch.zeros(8, 128, device="cuda")
     tiny_l = torch.zeros(8, device="cuda")
     ms_floor = timed(lambda: fbl.fb_merge(4, 128, tiny, tiny_l, tiny, tiny_l, tiny, tiny_l), 200)
@@ -330,6 +370,8 @@ def main() -> int:
         full_o.append(st0.o.float().clone())
     for s in range(w.steps):
         q, k, v = steps_dev[0][s]
+        if topk and s == 0:
+            select(0, q, 0)
         if args.policy == "fixed":
             st0.step(q, k, v, kp, vp, s, r, "cached", want_lse=False)
         else:
@@ -354,7 +396,6 @@ def main() -> int:
     lens = [int(lens[b + 1] - lens[b]) for b in range(w.batch)]
     sparse_tokens = None
     if args.sparse:
-        k_sel = int(st0.chunks.shape[-1])
         sparse_tokens = sum(min(64 * k_sel, l) for l in lens)   # selected keys per KV head, all streams
     pb, pf, bb, bf = algorithmic(w, lens, sparse_tokens)
     prefix_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
@@ -400,8 +441,10 @@ def main() -> int:
             "block_len": w.block_len, "prefix_len": lens if w.batch > 1 else lens[0],
             "denoise_steps": w.steps, "blocks": len(blocks), "refresh_period": r,
             "kv_layout": "head-major [Hkv][T][D]" if head_major else "token-major [T][Hkv][D]",
-            "sparse": (f"{int(st0.chunks.shape[-1])} of 64-token chunks per KV head selected; residual cached"
-                       if args.sparse else None),
+            "sparse": ({"chunks_kept": k_sel, "chunk_len": 64, "residual": "cached at refresh steps",
+                        "selection": ("top-k on the GPU at each block's first step (inside the step); pooled "
+                                      "chunk keys kept per layer, the block's new chunks pooled in the step" if topk
+                                      else "seeded random stand-in (fixed)")} if args.sparse else None),
             "step": "one block of denoise_steps attention steps, one layer",
             "policy": ({"name": "fixed", "refresh_period": r} if args.policy == "fixed" else
                        {"name": args.policy, "tau": args.tau, "eps": args.eps} if args.policy == "tau" else
@@ -419,7 +462,9 @@ def main() -> int:
                        "gbs": bb / (ms_block * 1e-3) / 1e9, "tflops": bf / (ms_block * 1e-3) / 1e12,
                        "mfma_frac": bf / (ms_block * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels_us": {"prefix_splitkv": ms_prefix_kernel * 1e3, "split_combine": ms_combine * 1e3,
-                       "block_attn_merge": ms_block * 1e3},
+                       "block_attn_merge": ms_block * 1e3,
+                       "select_chunks": ms_select * 1e3 if ms_select is not None else None,
+                       "select_chunks_full_pool": ms_select_full * 1e3 if ms_select_full is not None else None},
         "drift_max_abs": max(drift),
         "drift_per_step": drift,
         "sparse_only_drift_max_abs": max(sparse_only_drift) if sparse_only_drift else None,

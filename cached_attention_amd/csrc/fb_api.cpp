@@ -608,52 +608,31 @@ fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk
   return hip_status(fb::launch_append(a, stream), "block append launch");
 }
 
-size_t fb_select_chunks_ws(const fb_desc* d, int32_t chunk_len) {
-  clear_error();
-  if (check_desc(d) != FB_OK || check_offsets(d) != FB_OK) return 0;
-  if (chunk_len < 1) {
-    fail(FB_ERR_ARG, "chunk_len = %d < 1", chunk_len);
-    return 0;
-  }
-  int64_t total = 0;
-  for (int b = 0; b < d->batch; ++b)
-    total += ceil_div(d->prefix_offsets_host[b + 1] - d->prefix_offsets_host[b], chunk_len);
-  const size_t pooled = align_up((size_t)total * d->hkv * d->head_dim * sizeof(float));
-  const size_t scores = align_up((size_t)total * d->hkv * sizeof(float));
-  return std::max<size_t>(pooled + scores, kAlign);
-}
+}  // extern "C"
 
-fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pre, int32_t chunk_len, int32_t k,
-                           int32_t* chunk_idx_out, void* ws, size_t ws_bytes, void* stream) {
-  clear_error();
+// Chunk counts of the streams: n_max (and n_min) of ceil(Lp_b / chunk_len).
+static fb_status chunk_geometry(const fb_desc* d, int32_t chunk_len, int32_t* n_max, int32_t* n_min) {
   fb_status st = check_desc(d);
   if (st == FB_OK) st = check_offsets(d);
   if (st != FB_OK) return st;
   if (chunk_len < 1) return fail(FB_ERR_ARG, "chunk_len = %d < 1", chunk_len);
-  if (k < 1) return fail(FB_ERR_ARG, "k = %d < 1", k);
-  if (!q_blk || !k_pre || !chunk_idx_out) return fail(FB_ERR_NULL, "q_blk, k_pre and chunk_idx_out are required");
-  if (!aligned16(q_blk) || !aligned16(k_pre)) return fail(FB_ERR_ALIGN, "q_blk and k_pre must be 16-byte aligned");
-  int64_t total = 0, tiles = 0;
+  int64_t hi = 0, lo = INT64_MAX;
   for (int b = 0; b < d->batch; ++b) {
     const int64_t n = ceil_div(d->prefix_offsets_host[b + 1] - d->prefix_offsets_host[b], chunk_len);
-    if (n < k) return fail(FB_ERR_ARG, "stream %d has %lld chunks < k = %d", b, (long long)n, k);
-    if (n > fb::kMaxSelectChunks)
-      return fail(FB_ERR_SHAPE, "stream %d has %lld chunks > %d", b, (long long)n, fb::kMaxSelectChunks);
-    total += n;
-    tiles += (int64_t)d->hkv * ceil_div(n, 64);
+    hi = std::max(hi, n);
+    lo = std::min(lo, n);
   }
-  if (total * d->hkv > (1LL << 30) || tiles > (1LL << 30)) return fail(FB_ERR_SHAPE, "prefix too large");
-  const size_t pooled = align_up((size_t)total * d->hkv * d->head_dim * sizeof(float));
-  const size_t need = fb_select_chunks_ws(d, chunk_len);
-  st = check_ws(ws, ws_bytes, need);
-  if (st != FB_OK) return st;
-  fb::SelectArgs a;
+  if (hi * d->batch * d->hkv > (1LL << 30)) return fail(FB_ERR_SHAPE, "too many chunks");
+  *n_max = (int32_t)hi;
+  *n_min = (int32_t)lo;
+  return FB_OK;
+}
+
+static void fill_select(fb::SelectArgs& a, const fb_desc* d, int32_t chunk_len, int32_t chunk_cap, int32_t n_max) {
   memset(&a, 0, sizeof(a));
-  a.q = q_blk;
   a.q_sb = d->q_stride_b;
   a.q_st = d->q_stride_t;
   a.q_sh = d->q_stride_h;
-  a.k_pre = k_pre;
   a.pre_st = d->pre_stride_t;
   a.pre_sh = d->pre_stride_h;
   a.offsets = d->prefix_offsets_dev;
@@ -665,13 +644,98 @@ fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pr
   a.D = d->head_dim;
   a.dtype = d->dtype;
   a.chunk_len = chunk_len;
+  a.chunk_cap = chunk_cap;
+  a.max_chunks = n_max;
+}
+
+static fb_status select_checks(const fb_desc* d, int32_t k, int32_t n_max, int32_t n_min, const void* q_blk,
+                               const void* idx) {
+  if (k < 1) return fail(FB_ERR_ARG, "k = %d < 1", k);
+  if (n_min < k) return fail(FB_ERR_ARG, "a stream has %d chunks < k = %d", n_min, k);
+  if (n_max > fb::kMaxSelectChunks) return fail(FB_ERR_SHAPE, "a stream has %d chunks > %d", n_max, fb::kMaxSelectChunks);
+  if (!q_blk || !idx) return fail(FB_ERR_NULL, "q_blk and chunk_idx_out are required");
+  if (!aligned16(q_blk)) return fail(FB_ERR_ALIGN, "q_blk must be 16-byte aligned");
+  (void)d;
+  return FB_OK;
+}
+
+static size_t pooled_bytes(const fb_desc* d, int32_t cap) {
+  return align_up((size_t)d->batch * cap * d->hkv * d->head_dim * sizeof(float));
+}
+
+extern "C" {
+
+size_t fb_select_chunks_ws(const fb_desc* d, int32_t chunk_len) {
+  clear_error();
+  int32_t n_max = 0, n_min = 0;
+  if (chunk_geometry(d, chunk_len, &n_max, &n_min) != FB_OK) return 0;
+  const size_t scores = align_up((size_t)d->batch * d->hkv * n_max * sizeof(float));
+  return std::max<size_t>(pooled_bytes(d, n_max) + scores, kAlign);
+}
+
+fb_status fb_pool_chunk_keys(const fb_desc* d, const void* k_pre, int32_t chunk_len, int32_t chunk_cap,
+                             int32_t first_chunk, float* pooled, void* stream) {
+  clear_error();
+  int32_t n_max = 0, n_min = 0;
+  fb_status st = chunk_geometry(d, chunk_len, &n_max, &n_min);
+  if (st != FB_OK) return st;
+  if (chunk_cap < n_max) return fail(FB_ERR_ARG, "chunk_cap = %d < %d chunks of the longest stream", chunk_cap, n_max);
+  if (first_chunk < 0) return fail(FB_ERR_ARG, "first_chunk = %d < 0", first_chunk);
+  if (!k_pre || !pooled) return fail(FB_ERR_NULL, "k_pre and pooled are required");
+  if (!aligned16(k_pre) || !aligned16(pooled)) return fail(FB_ERR_ALIGN, "k_pre and pooled must be 16-byte aligned");
+  if (first_chunk >= n_max) return FB_OK;
+  fb::SelectArgs a;
+  fill_select(a, d, chunk_len, chunk_cap, n_max);
+  a.k_pre = k_pre;
+  a.first_chunk = first_chunk;
+  a.pooled = pooled;
+  return hip_status(fb::launch_pool(a, stream), "chunk pooling launch");
+}
+
+fb_status fb_select_chunks_pooled(const fb_desc* d, const void* q_blk, const float* pooled, int32_t chunk_len,
+                                  int32_t chunk_cap, int32_t k, float* scores, int32_t* chunk_idx_out,
+                                  void* stream) {
+  clear_error();
+  int32_t n_max = 0, n_min = 0;
+  fb_status st = chunk_geometry(d, chunk_len, &n_max, &n_min);
+  if (st == FB_OK) st = select_checks(d, k, n_max, n_min, q_blk, chunk_idx_out);
+  if (st != FB_OK) return st;
+  if (chunk_cap < n_max) return fail(FB_ERR_ARG, "chunk_cap = %d < %d chunks of the longest stream", chunk_cap, n_max);
+  if (!pooled || !scores) return fail(FB_ERR_NULL, "pooled and scores are required");
+  if (!aligned16(pooled)) return fail(FB_ERR_ALIGN, "pooled must be 16-byte aligned");
+  fb::SelectArgs a;
+  fill_select(a, d, chunk_len, chunk_cap, n_max);
+  a.q = q_blk;
   a.k = k;
-  a.total_chunks = (int32_t)total;
-  a.work_tiles = (int32_t)tiles;
-  a.pooled = (float*)ws;
-  a.scores = (float*)((char*)ws + pooled);
+  a.pooled = (float*)pooled;
+  a.scores = scores;
   a.idx_out = chunk_idx_out;
-  return hip_status(fb::launch_select(a, stream), "chunk selection launch");
+  return hip_status(fb::launch_select_pooled(a, stream), "chunk selection launch");
+}
+
+fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pre, int32_t chunk_len, int32_t k,
+                           int32_t* chunk_idx_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  int32_t n_max = 0, n_min = 0;
+  fb_status st = chunk_geometry(d, chunk_len, &n_max, &n_min);
+  if (st == FB_OK) st = select_checks(d, k, n_max, n_min, q_blk, chunk_idx_out);
+  if (st != FB_OK) return st;
+  if (!k_pre) return fail(FB_ERR_NULL, "k_pre is required");
+  if (!aligned16(k_pre)) return fail(FB_ERR_ALIGN, "k_pre must be 16-byte aligned");
+  const size_t need = fb_select_chunks_ws(d, chunk_len);
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+  fb::SelectArgs a;
+  fill_select(a, d, chunk_len, n_max, n_max);
+  a.q = q_blk;
+  a.k_pre = k_pre;
+  a.k = k;
+  a.pooled = (float*)ws;
+  a.scores = (float*)((char*)ws + pooled_bytes(d, n_max));
+  a.idx_out = chunk_idx_out;
+  int rc = fb::launch_pool(a, stream);
+  if (rc == 0) rc = fb::launch_select_pooled(a, stream);
+  return hip_status(rc, "chunk selection launch");
 }
 
 }  // extern "C"

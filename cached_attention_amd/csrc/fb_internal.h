@@ -152,7 +152,7 @@ struct AppendArgs {
 };
 int launch_append(const AppendArgs& a, void* stream);
 // chunk selection for the sparse variant: pooled chunk keys, max query score, top-k
-constexpr int kMaxSelectChunks = 16384;   // chunks per stream the top-k pass sorts in LDS
+constexpr int kMaxSelectChunks = 16384;   // chunks per stream the top-k pass holds in LDS
 struct SelectArgs {
   const void* q;
   int64_t q_sb, q_st, q_sh;
@@ -160,13 +160,15 @@ struct SelectArgs {
   int64_t pre_st, pre_sh;
   const int64_t* offsets;   // device [B+1]
   int32_t B, Hq, Hkv, G, Lb, D, dtype, chunk_len, k;
-  int32_t total_chunks;     // sum over streams of ceil(Lp_b / chunk_len)
-  int32_t work_tiles;       // sum over streams of Hkv * ceil(n_b / 64)
-  float* pooled;            // [total_chunks][Hkv][D]
-  float* scores;            // [total_chunks][Hkv]
+  int32_t chunk_cap;        // chunk capacity per stream of pooled / scores
+  int32_t max_chunks;       // max over streams of ceil(Lp_b / chunk_len)
+  int32_t first_chunk;      // pooling: chunks first_chunk .. of every stream
+  float* pooled;            // [B][chunk_cap][Hkv][D]
+  float* scores;            // [B][Hkv][chunk_cap]
   int32_t* idx_out;         // [B][Hkv][k]
 };
-int launch_select(const SelectArgs& a, void* stream);
+int launch_pool(const SelectArgs& a, void* stream);
+int launch_select_pooled(const SelectArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
 
 }  // namespace fb

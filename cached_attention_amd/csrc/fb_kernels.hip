@@ -1056,53 +1056,193 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
 // ---------------------------------------------------------------------------
 // chunk selection for the sparse variant (pooled key, max query score, top-k)
 // ---------------------------------------------------------------------------
+//
+// Pooled keys live in [B][chunk_cap][Hkv][D] fp32, scores in [B][Hkv][chunk_cap]
+// fp32, so that a caller can keep the pooled keys of an append-only prefix
+// and pool only the chunks a new block touched.
 
 __device__ __forceinline__ int chunks_of(const int64_t* off, int b, int cl) {
   return (int)((prefix_len(off, b) + cl - 1) / cl);
 }
 
-// one wave per (chunk, KV head): the mean of the chunk's keys (fp32 sums)
-__global__ void __launch_bounds__(256) pool_kernel(const SelectArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= (int64_t)a.total_chunks * a.Hkv) return;
-  const int gc = (int)(w / a.Hkv), g = (int)(w % a.Hkv);
-  int b = 0, acc = 0;
-  for (; b < a.B; ++b) {
-    const int n = chunks_of(a.offsets, b, a.chunk_len);
-    if (gc < acc + n) break;
-    acc += n;
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// one wave per (stream, chunk, KV head): the mean of the chunk's keys in fp32.
+// A lane loads 16 bytes of a key row, so one load instruction covers 64 / P
+// rows (P = 16-byte pieces per row); four such loads are in flight at once.
+template <int D, typename T>
+__device__ __forceinline__ void pool_chunk(const SelectArgs& a, int b, int c, int g, int lane) {
+  constexpr int EPP = 16 / (int)sizeof(T);
+  constexpr int P = D / EPP;
+  constexpr int RPL = 64 / P;
+  typedef T vecT __attribute__((ext_vector_type(EPP)));
+  const int64_t s1 = ld_const(a.offsets, b + 1);
+  const int64_t t0 = ld_const(a.offsets, b) + (int64_t)c * a.chunk_len;
+  const int64_t t1 = min(t0 + a.chunk_len, s1);
+  const int row = lane / P, piece = lane % P;
+  const T* base = (const T*)a.k_pre + (int64_t)g * a.pre_sh + piece * EPP;
+  float acc[EPP];
+#pragma unroll
+  for (int j = 0; j < EPP; ++j) acc[j] = 0.f;
+  int64_t t = t0 + row;
+  for (; t + 3 * RPL < t1; t += 4 * RPL) {
+    vecT v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *(const vecT*)(base + (t + u * RPL) * a.pre_st);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < EPP; ++j) acc[j] += to_f32(v[u][j]);
   }
-  const int64_t s0 = ld_const(a.offsets, b);
-  const int64_t t0 = s0 + (int64_t)(gc - acc) * a.chunk_len;
-  const int64_t t1 = min(t0 + a.chunk_len, ld_const(a.offsets, b + 1));
-  const float inv = 1.f / (float)(t1 - t0);
-  for (int d = lane; d < a.D; d += 64) {
-    float sum = 0.f;
-    for (int64_t t = t0; t < t1; ++t) sum += ld_elem(a.k_pre, t * a.pre_st + (int64_t)g * a.pre_sh + d, a.dtype);
-    a.pooled[((int64_t)gc * a.Hkv + g) * a.D + d] = sum * inv;
+  for (; t < t1; t += RPL) {
+    const vecT v = *(const vecT*)(base + t * a.pre_st);
+#pragma unroll
+    for (int j = 0; j < EPP; ++j) acc[j] += to_f32(v[j]);
+  }
+#pragma unroll
+  for (int o = P; o < 64; o <<= 1)
+#pragma unroll
+    for (int j = 0; j < EPP; ++j) acc[j] += shfl_xor_f(acc[j], o);
+  if (lane < P) {
+    const float inv = 1.f / (float)(t1 - t0);
+    float* dst = a.pooled + (((int64_t)b * a.chunk_cap + c) * a.Hkv + g) * D + piece * EPP;
+#pragma unroll
+    for (int j = 0; j < EPP; j += 4) *(f32x4*)(dst + j) = (f32x4){acc[j] * inv, acc[j + 1] * inv,
+                                                                  acc[j + 2] * inv, acc[j + 3] * inv};
   }
 }
 
-// one workgroup per (stream, KV head, 64 chunks); four threads per chunk
-// split the group's query rows, then the max over them
-template <int D>
-__device__ void score_tile(const SelectArgs& a) {
-  int w = blockIdx.x, b = 0, base = 0;
-  for (; b < a.B; ++b) {
-    const int n = chunks_of(a.offsets, b, a.chunk_len);
-    const int tiles = a.Hkv * ((n + 63) / 64);
-    if (w < tiles) break;
-    w -= tiles;
-    base += n;
+// grid: 4 waves per workgroup over (stream, chunk first_chunk.., KV head)
+__global__ void __launch_bounds__(256) pool_kernel(const SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int span = a.max_chunks - a.first_chunk;
+  if (w >= (int64_t)a.B * span * a.Hkv) return;
+  const int g = (int)(w % a.Hkv);
+  const int64_t r = w / a.Hkv;
+  const int c = a.first_chunk + (int)(r % span), b = (int)(r / span);
+  if (c >= chunks_of(a.offsets, b, a.chunk_len)) return;
+  if (a.dtype == kDtypeBf16) {
+    if (a.D == 128) pool_chunk<128, __bf16>(a, b, c, g, lane); else pool_chunk<64, __bf16>(a, b, c, g, lane);
+  } else {
+    if (a.D == 128) pool_chunk<128, float>(a, b, c, g, lane); else pool_chunk<64, float>(a, b, c, g, lane);
   }
-  const int n = chunks_of(a.offsets, b, a.chunk_len);
-  const int per_g = (n + 63) / 64;
-  const int g = w / per_g, tile = w % per_g;
-  const int c = tile * 64 + (threadIdx.x >> 2), sub = threadIdx.x & 3;
-  float kk[D];
+}
+
+// x == hi + mid + lo exactly: each bf16 term takes the next 8 significand bits
+__device__ __forceinline__ void split3(const float* x, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)x[j];
+    const float r1 = x[j] - (float)h;
+    const __bf16 m = (__bf16)r1;
+    hi[j] = h;
+    mid[j] = m;
+    lo[j] = (__bf16)(r1 - (float)m);
+  }
+}
+
+// bf16 queries: S[q row][chunk] = Q . pooled on MFMA, the fp32 pooled key
+// split into three bf16 terms.  bf16 x bf16 products are exact in fp32, so
+// the score carries fp32 accumulation error only.  A workgroup scores 64
+// chunks, 16 per wave (B operand columns, held in registers), against all
+// G*Lb query rows of its KV head (A operand), which pass through LDS in
+// 64-row rounds shared by the four waves: the next round's rows are loaded
+// into registers while the current round's MFMAs run.  LDS row of 2D bytes,
+// 16-byte slot j of row r stored at slot j ^ (r mod slots-per-row), so the 16
+// rows read by one fragment load fall on distinct banks.
+template <int D>
+__device__ __forceinline__ void score_mfma(const SelectArgs& a, int b, int g, int c_wg, int n) {
+  constexpr int KS = D / 32, SLOTS = D / 8, ROWB = 2 * D;
+  constexpr int PER = 64 * SLOTS / 256;   // 16-byte slots staged per thread per round
+  __shared__ __attribute__((aligned(16))) char qs[2][64 * ROWB];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, lg = lane >> 4, wave = tid >> 6;
+  const int c = c_wg + wave * 16 + l16;
+  bf16x8 kh[KS], km[KS], kl[KS];
+  if (c < n) {
+    const float* pk = a.pooled + (((int64_t)b * a.chunk_cap + c) * a.Hkv + g) * D + lg * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x4 x0 = *(const f32x4*)(pk + ks * 32), x1 = *(const f32x4*)(pk + ks * 32 + 4);
+      const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      split3(x, kh[ks], km[ks], kl[ks]);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kh[ks] = km[ks] = kl[ks] = (bf16x8){};
+  }
+  const int rows = a.G * a.Lb;
+  const int rounds = (rows + 63) / 64;
+  u32x4 stage[PER];
+  auto load = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j, row = r * 64 + i / SLOTS, slot = i % SLOTS;
+      if (row < rows) {
+        const int h = g * a.G + row / a.Lb, pos = row % a.Lb;
+        stage[j] = *(const u32x4*)((const __bf16*)a.q + (int64_t)b * a.q_sb + (int64_t)pos * a.q_st +
+                                   (int64_t)h * a.q_sh + slot * 8);
+      } else {
+        stage[j] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j, rr = i / SLOTS, slot = i % SLOTS;
+      *(u32x4*)(qs[buf] + rr * ROWB + ((slot ^ (rr & (SLOTS - 1))) * 16)) = stage[j];
+    }
+  };
+  load(0);
+  store(0);
+  __syncthreads();
+  float best = kNegInf;
+  for (int r = 0; r < rounds; ++r) {
+    if (r + 1 < rounds) load(r + 1);
+    bf16x8 qa[4][KS];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int rr = rt * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[rt][ks] = *(const bf16x8*)(qs[r & 1] + rr * ROWB + (((ks * 4 + lg) ^ (rr & (SLOTS - 1))) * 16));
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kl[ks], acc[rt], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], km[ks], acc[rt], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rt][ks], kh[ks], acc[rt], 0, 0, 0);
+    }
+    // accumulator element i of lane (l16, lg): query row 4*lg + i of the tile, chunk l16
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (r * 64 + rt * 16 + 4 * lg + i < rows) best = fmaxf(best, acc[rt][i]);
+    if (r + 1 < rounds) store((r + 1) & 1);
+    __syncthreads();
+  }
+  best = fmaxf(best, shfl_xor_f(best, 16));
+  best = fmaxf(best, shfl_xor_f(best, 32));
+  if (lg == 0 && c < n) a.scores[((int64_t)b * a.Hkv + g) * a.chunk_cap + c] = best;
+}
+
+// fp32 queries: plain fp32 dot products, four lanes per chunk splitting the
+// query rows, then the max over them
+template <int D>
+__device__ __forceinline__ void score_f32(const SelectArgs& a, int b, int g, int tile0, int n) {
+  const int c = tile0 + (threadIdx.x >> 2), sub = threadIdx.x & 3;
   const bool live = c < n;
-  const float* pk = a.pooled + ((int64_t)(base + (live ? c : 0)) * a.Hkv + g) * D;
+  const float* pk = a.pooled + (((int64_t)b * a.chunk_cap + (live ? c : 0)) * a.Hkv + g) * D;
+  float kk[D];
 #pragma unroll
   for (int d = 0; d < D; d += 4) {
     const f32x4 v = *(const f32x4*)(pk + d);
@@ -1112,102 +1252,140 @@ __device__ void score_tile(const SelectArgs& a) {
   const int rows = a.G * a.Lb;
   for (int r = sub; r < rows; r += 4) {
     const int h = g * a.G + r / a.Lb, pos = r % a.Lb;
-    const int64_t qo = (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh;
+    const float* qp = (const float*)a.q + (int64_t)b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh;
     float dot = 0.f;
-    if (a.dtype == kDtypeBf16) {
-      const __bf16* qp = (const __bf16*)a.q + qo;
 #pragma unroll
-      for (int d = 0; d < D; d += 8) {
-        const bf16x8 qv = *(const bf16x8*)(qp + d);
+    for (int d = 0; d < D; d += 4) {
+      const f32x4 qv = *(const f32x4*)(qp + d);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dot = __builtin_fmaf((float)qv[j], kk[d + j], dot);
-      }
-    } else {
-      const float* qp = (const float*)a.q + qo;
-#pragma unroll
-      for (int d = 0; d < D; d += 4) {
-        const f32x4 qv = *(const f32x4*)(qp + d);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dot = __builtin_fmaf(qv[j], kk[d + j], dot);
-      }
+      for (int j = 0; j < 4; ++j) dot = __builtin_fmaf(qv[j], kk[d + j], dot);
     }
     best = fmaxf(best, dot);
   }
-  best = fmaxf(best, __shfl_xor(best, 1, 64));
-  best = fmaxf(best, __shfl_xor(best, 2, 64));
-  if (live && sub == 0) a.scores[(int64_t)(base + c) * a.Hkv + g] = best;
+  best = fmaxf(best, shfl_xor_f(best, 1));
+  best = fmaxf(best, shfl_xor_f(best, 2));
+  if (live && sub == 0) a.scores[((int64_t)b * a.Hkv + g) * a.chunk_cap + c] = best;
 }
 
+// one workgroup per (stream, KV head, 64 chunks)
+template <bool BF16>
 __global__ void __launch_bounds__(256) score_kernel(const SelectArgs a) {
-  if (a.D == 128)
-    score_tile<128>(a);
-  else
-    score_tile<64>(a);
-}
-
-// sortable key: ascending order = descending score, then ascending chunk
-__device__ __forceinline__ uint64_t topk_key(float s, int i) {
-  uint32_t u = __builtin_bit_cast(uint32_t, s);
-  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)(~asc) << 32) | (uint32_t)i;
-}
-
-// one workgroup per (stream, KV head): bitonic sort of the chunk keys in
-// LDS, flag the first k, write the flagged chunk indices in ascending order
-__global__ void __launch_bounds__(1024) topk_kernel(const SelectArgs a) {
-  __shared__ uint64_t keys[kMaxSelectChunks];
-  __shared__ unsigned char flag[kMaxSelectChunks];
-  __shared__ int wsum[16];
-  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
-  const int tid = threadIdx.x;
-  int base = 0;
-  for (int bb = 0; bb < b; ++bb) base += chunks_of(a.offsets, bb, a.chunk_len);
+  constexpr int CPW = 64;
+  const int tiles = (a.max_chunks + CPW - 1) / CPW;
+  const int tile = blockIdx.x % tiles;
+  const int g = (blockIdx.x / tiles) % a.Hkv, b = blockIdx.x / tiles / a.Hkv;
   const int n = chunks_of(a.offsets, b, a.chunk_len);
-  int P = 2;
-  while (P < n) P <<= 1;
-  for (int i = tid; i < P; i += 1024) {
-    keys[i] = i < n ? topk_key(a.scores[(int64_t)(base + i) * a.Hkv + g], i) : ~0ull;
-    if (i < n) flag[i] = 0;
+  if (tile * CPW >= n) return;   // uniform over the workgroup
+  if constexpr (BF16) {
+    if (a.D == 128) score_mfma<128>(a, b, g, tile * CPW, n); else score_mfma<64>(a, b, g, tile * CPW, n);
+  } else {
+    if (a.D == 128) score_f32<128>(a, b, g, tile * CPW, n); else score_f32<64>(a, b, g, tile * CPW, n);
   }
-  __syncthreads();
-  for (int k2 = 2; k2 <= P; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += 1024) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool up = (i & k2) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int j = tid; j < a.k; j += 1024) flag[(uint32_t)keys[j]] = 1;
-  __syncthreads();
-  // compaction in index order: each thread owns a contiguous run of chunks
-  const int per = (n + 1023) / 1024;
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  int cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += flag[i];
-  const int lane = tid & 63, wave = tid >> 6;
-  int incl = cnt;
+}
+
+// order key: ascending order = descending score (-0 counted as +0)
+__device__ __forceinline__ uint32_t rank_key(float s) {
+  if (s == 0.f) s = 0.f;
+  const uint32_t u = __builtin_bit_cast(uint32_t, s);
+  return ~((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+}
+
+// exclusive prefix sum of v over the 1024 threads of the workgroup
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
+  __syncthreads();   // wsum free from any earlier use
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int before = 0;
   for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
-  int pos = before + incl - cnt;
+  return before + incl - v;
+}
+
+// one workgroup per (stream, KV head): radix select of the k-th best order
+// key (four 8-bit digits, most significant first), then the chunks strictly
+// better plus the lowest-index chunks tied with it, written ascending
+__global__ void __launch_bounds__(1024) topk_kernel(const SelectArgs a) {
+  __shared__ uint32_t keys[kMaxSelectChunks];
+  __shared__ int hist[256];
+  __shared__ int wsum[16];
+  __shared__ uint32_t sel_prefix;
+  __shared__ int sel_rank;
+  const int b = blockIdx.x / a.Hkv, g = blockIdx.x % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = chunks_of(a.offsets, b, a.chunk_len);
+  const float* sc = a.scores + ((int64_t)b * a.Hkv + g) * a.chunk_cap;
+  for (int i = tid; i < n; i += 1024) keys[i] = rank_key(sc[i]);
+  if (tid == 0) {
+    sel_prefix = 0;
+    sel_rank = a.k;   // 1-based rank of the wanted key among those matching the prefix
+  }
+  uint32_t mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    const uint32_t prefix = sel_prefix;
+    for (int i = tid; i < n; i += 1024) {
+      const uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {   // wave 0: the digit whose cumulative count reaches the rank
+      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int sum4 = h0 + h1 + h2 + h3;
+      int incl = sum4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const int rank = sel_rank;
+      const int excl = incl - sum4;
+      if (excl < rank && rank <= incl) {   // exactly one lane
+        int cum = excl, d = 4 * lane;
+        const int hs[4] = {h0, h1, h2, h3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (d == 4 * lane + j && rank > cum + hs[j]) {
+            cum += hs[j];
+            d = 4 * lane + j + 1;
+          }
+        }
+        sel_prefix = prefix | ((uint32_t)d << shift);
+        sel_rank = rank - cum;
+      }
+    }
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t thr = sel_prefix;   // the k-th best key
+  const int ties_wanted = sel_rank;  // how many keys equal to it are kept (lowest indices)
+  // compaction in index order over contiguous runs of chunks per thread
+  const int per = (n + 1023) / 1024;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int ties = 0;
+  for (int i = i0; i < i1; ++i) ties += keys[i] == thr;
+  int tie_rank = wg_exclusive_scan(ties, wsum);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = keys[i];
+    if (key < thr) ++cnt;
+    else if (key == thr) cnt += tie_rank++ < ties_wanted;
+  }
+  int pos = wg_exclusive_scan(cnt, wsum);
+  tie_rank -= ties;
   int32_t* out = a.idx_out + ((int64_t)b * a.Hkv + g) * a.k;
-  for (int i = i0; i < i1; ++i)
-    if (flag[i]) out[pos++] = i;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = keys[i];
+    bool take = key < thr;
+    if (key == thr) take = tie_rank++ < ties_wanted;
+    if (take) out[pos++] = i;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1282,11 +1460,22 @@ int launch_append(const AppendArgs& a, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_select(const SelectArgs& a, void* stream) {
+int launch_pool(const SelectArgs& a, void* stream) {
+  const int64_t waves = (int64_t)a.B * (a.max_chunks - a.first_chunk) * a.Hkv;
+  if (waves <= 0) return 0;
+  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_select_pooled(const SelectArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  const int64_t waves = (int64_t)a.total_chunks * a.Hkv;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(score_kernel, dim3((unsigned)a.work_tiles), dim3(256), 0, s, a);
+  if (a.dtype == kDtypeBf16) {
+    const int64_t tiles = (int64_t)a.B * a.Hkv * ((a.max_chunks + 63) / 64);
+    hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  } else {
+    const int64_t tiles = (int64_t)a.B * a.Hkv * ((a.max_chunks + 63) / 64);
+    hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((int64_t)a.B * a.Hkv)), dim3(1024), 0, s, a);
   return (int)hipGetLastError();
 }

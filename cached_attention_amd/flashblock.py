@@ -26,6 +26,7 @@ FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
            "fb_block_attn", "fb_merge", "fb_step", "fb_refresh_mask_tau", "fb_refresh_mask_gamma",
            "fb_step_masked", "fb_append_block", "fb_select_chunks_ws", "fb_select_chunks",
+           "fb_pool_chunk_keys", "fb_select_chunks_pooled",
            "fb_status_string", "fb_last_error", "fb_abi_version")
 
 
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
         l.fb_select_chunks_ws.restype = sz
         l.fb_select_chunks.argtypes = [D, P, P, i32, i32, P, P, sz, P]
         l.fb_select_chunks.restype = i32
+        l.fb_pool_chunk_keys.argtypes = [D, P, i32, i32, i32, P, P]
+        l.fb_pool_chunk_keys.restype = i32
+        l.fb_select_chunks_pooled.argtypes = [D, P, P, i32, i32, i32, P, P, P]
+        l.fb_select_chunks_pooled.restype = i32
         l.fb_status_string.argtypes = [i32]
         l.fb_status_string.restype = ctypes.c_char_p
         l.fb_last_error.argtypes = []
@@ -263,6 +268,18 @@ def fb_select_chunks(desc: Desc, q_blk, k_pre, chunk_len: int, k: int, chunk_idx
                      stream=None) -> None:
     _check(lib().fb_select_chunks(desc.ref, _ptr(q_blk), _ptr(k_pre), chunk_len, k, _ptr(chunk_idx_out), _ptr(ws),
                                   ws_bytes, _stream(stream)), "fb_select_chunks")
+
+
+def fb_pool_chunk_keys(desc: Desc, k_pre, chunk_len: int, chunk_cap: int, first_chunk: int, pooled,
+                       stream=None) -> None:
+    _check(lib().fb_pool_chunk_keys(desc.ref, _ptr(k_pre), chunk_len, chunk_cap, first_chunk, _ptr(pooled),
+                                    _stream(stream)), "fb_pool_chunk_keys")
+
+
+def fb_select_chunks_pooled(desc: Desc, q_blk, pooled, chunk_len: int, chunk_cap: int, k: int, scores,
+                            chunk_idx_out, stream=None) -> None:
+    _check(lib().fb_select_chunks_pooled(desc.ref, _ptr(q_blk), _ptr(pooled), chunk_len, chunk_cap, k, _ptr(scores),
+                                         _ptr(chunk_idx_out), _stream(stream)), "fb_select_chunks_pooled")
 
 
 def fb_status_string(status: int) -> str:

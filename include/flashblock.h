@@ -227,14 +227,33 @@ fb_status fb_append_block(const fb_desc* d, const void* k_blk, const void* v_blk
  * one is the plainest block-level rule: each chunk of chunk_len prefix tokens
  * is represented by the mean of its keys (fp32), scored for a (stream, KV
  * head) by the largest dot product of that KV head's block queries with it,
- * and the k best chunks are kept (ties to the lower chunk index).  Writes
- * chunk_idx_out [B][Hkv][k] int32, ascending per (stream, KV head) -- the
- * fb_sparse chunk list.  Every stream needs at least k and at most 16384
- * chunks.  ws: fb_select_chunks_ws(d, chunk_len) bytes, 256-byte aligned
- * (pooled keys [chunks][Hkv][D] fp32, then scores [chunks][Hkv] fp32). */
+ * and the k best chunks are kept (ties to the lower chunk index).  The chunk
+ * list written is chunk_idx_out [B][Hkv][k] int32, ascending per (stream, KV
+ * head) -- the fb_sparse chunk list.  Every stream needs at least k and at
+ * most 16384 chunks; otherwise FB_ERR_ARG / FB_ERR_SHAPE.
+ *
+ * One-shot form: fb_select_chunks pools every chunk and selects.  ws holds
+ * fb_select_chunks_ws(d, chunk_len) bytes, 256-byte aligned (pooled keys
+ * [B][n_max][Hkv][D] fp32, then scores [B][Hkv][n_max] fp32, n_max = chunks
+ * of the longest stream); fb_select_chunks_ws returns 0 on a bad desc. */
 size_t fb_select_chunks_ws(const fb_desc* d, int32_t chunk_len);
 fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pre, int32_t chunk_len, int32_t k,
                            int32_t* chunk_idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Two-call form for an append-only prefix, whose chunk means do not change
+ * once a chunk is full.  pooled: caller-owned fp32 [B][chunk_cap][Hkv][D]
+ * (16-byte aligned), kept across blocks; chunk_cap >= chunks of the longest
+ * stream.  fb_pool_chunk_keys (re)computes chunks first_chunk, first_chunk+1,
+ * ... of every stream from k_pre (fb_desc prefix strides) and leaves lower
+ * chunks untouched: after appending a block, first_chunk = the smallest old
+ * stream length / chunk_len (rounded down) re-pools the partial last chunk
+ * and pools the new ones.  fb_select_chunks_pooled scores and selects from
+ * pooled; scores is caller-owned fp32 [B][Hkv][chunk_cap] scratch. */
+fb_status fb_pool_chunk_keys(const fb_desc* d, const void* k_pre, int32_t chunk_len, int32_t chunk_cap,
+                             int32_t first_chunk, float* pooled, void* stream);
+fb_status fb_select_chunks_pooled(const fb_desc* d, const void* q_blk, const float* pooled, int32_t chunk_len,
+                                  int32_t chunk_cap, int32_t k, float* scores, int32_t* chunk_idx_out,
+                                  void* stream);
 
 const char* fb_status_string(fb_status s);
 const char* fb_last_error(void);

@@ -179,3 +179,26 @@ def test_select_chunks_validation():
     assert lib.fb_select_chunks_ws(d.ref, 0) == 0 and fbl.fb_last_error() != ""
     with pytest.raises(fbl.FlashBlockError):
         fbl.fb_select_chunks_ws(d, 0)
+
+
+def test_pool_and_select_pooled_validation():
+    d = _desc()   # 2048 chunks of 64
+    lib = fbl.lib()
+    pool = lambda **kw: lib.fb_pool_chunk_keys(d.ref, kw.get("kp", FAKE), kw.get("cl", 64), kw.get("cap", 2048),
+                                               kw.get("first", 0), kw.get("pooled", FAKE), None)
+    assert pool(cap=2047) == fbl.FB_ERR_ARG
+    assert pool(first=-1) == fbl.FB_ERR_ARG
+    assert pool(cl=0) == fbl.FB_ERR_ARG
+    assert pool(pooled=None) == fbl.FB_ERR_NULL
+    assert pool(pooled=FAKE + 4) == fbl.FB_ERR_ALIGN
+    assert pool(first=2048) == fbl.FB_OK            # nothing left to pool: no launch
+    sp = lambda **kw: lib.fb_select_chunks_pooled(d.ref, kw.get("q", FAKE), kw.get("pooled", FAKE), 64,
+                                                  kw.get("cap", 2048), kw.get("k", 205), kw.get("sc", FAKE),
+                                                  kw.get("idx", FAKE), None)
+    assert sp(cap=100) == fbl.FB_ERR_ARG
+    assert sp(k=0) == fbl.FB_ERR_ARG
+    assert sp(k=4096) == fbl.FB_ERR_ARG
+    assert sp(sc=None) == fbl.FB_ERR_NULL
+    assert sp(pooled=None) == fbl.FB_ERR_NULL
+    assert sp(pooled=FAKE + 8) == fbl.FB_ERR_ALIGN
+    assert sp(q=FAKE + 2) == fbl.FB_ERR_ALIGN
