@@ -128,6 +128,8 @@ def main() -> int:
     ap.add_argument("--sparse", action="store_true",
                     help="chunk-sparse variant: cached residual of the unselected 64-token chunks plus a fresh "
                          "partial over the selected ones (workloads with a sparse keep fraction)")
+    ap.add_argument("--density", type=float, default=0.0,
+                    help="sparse variant: fraction of 64-token chunks kept (default: the workload's, 10%%)")
     ap.add_argument("--chunk-select", choices=("topk", "random"), default="topk",
                     help="sparse variant: chunks chosen on the GPU from each block's first-step queries "
                          "(pooled chunk keys, max query score, top-k), or a fixed seeded random stand-in")
@@ -176,6 +178,11 @@ def main() -> int:
     w = wl.WORKLOADS[args.workload]
     if args.prefix_len > 0:
         w = dataclasses.replace(w, name=f"{w.name}@{args.prefix_len}", prefix_len=args.prefix_len)
+    if args.density > 0:
+        if not 0 < args.density <= 1 or not args.sparse:
+            print("--density takes a fraction in (0, 1] with --sparse", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, name=f"{w.name}~{args.density:g}", sparse_keep=args.density)
     r = args.r
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     log(f"[bench] workload {w.name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} D={w.head_dim} Lb={w.block_len} "
