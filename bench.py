@@ -88,7 +88,7 @@ def blas_threads() -> int:
     return 1
 
 
-def cpu_baseline(w, prefix, blocks, r, budget_s=12.0):
+def cpu_baseline(w, prefix, blocks, r, budget_s=15.0):
     """The fp64 oracle (as it stands) on the same workload's first block in
     cached mode, on the host cores; repeated until ~budget_s of CPU work."""
     import oracle
@@ -102,7 +102,7 @@ def cpu_baseline(w, prefix, blocks, r, budget_s=12.0):
         oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r)
         runs += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or runs >= 20:
+        if el >= budget_s or runs >= 100:
             break
     per_block = el / runs
     tok = w.batch * w.block_len * w.steps
