@@ -63,6 +63,43 @@ def measured_traffic(workload):
     return None
 
 
+def smi_snapshot():
+    """Socket power and clocks of GPU 0 from `amd-smi metric` (a child process), or None."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    try:
+        out = subprocess.run([exe, "metric", "-g", "0", "--power", "--clock", "--json"], capture_output=True,
+                             text=True, timeout=30).stdout
+        d = json.loads(out[out.index("{"):])
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = g["clock"]
+        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_") and isinstance(clk[k], dict)]
+        return {"socket_power_w": g["power"]["socket_power"]["value"], "gfx_clk_mhz": gfx,
+                "gfx_clk_max_mhz": clk["gfx_0"]["max_clk"]["value"], "mem_clk_mhz": clk["mem_0"]["clk"]["value"]}
+    except Exception:
+        return None
+
+
+def snapshot_under_load(fn, sync, seconds=3.0, lead=1.0):
+    """amd-smi snapshot started `lead` seconds into a run of fn back to back
+    (untimed), which lasts at least `seconds` and until the snapshot returns."""
+    import threading
+    res = {}
+    t = threading.Thread(target=lambda: res.update(snap=smi_snapshot()))
+    t0 = time.perf_counter()
+    started = False
+    while not started or t.is_alive() or time.perf_counter() < t0 + seconds:
+        for _ in range(10):
+            fn()
+        sync()
+        if not started and time.perf_counter() >= t0 + lead:
+            t.start()
+            started = True
+    t.join()
+    return res.get("snap")
+
+
 def algorithmic(w, lens, sparse_tokens=None):
     """Algorithmic bytes / flops of the prefix pass and of the in-block + merge pass."""
     e = 2 if w.dtype == "bf16" else 4
@@ -292,6 +329,7 @@ def main() -> int:
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n   # ms
 
+    gpu_idle = smi_snapshot()
     # ---- whole bench steps: cached (r) and full recompute ----
     for _ in range(args.warmup):
         bench_step("cached", r)
@@ -300,6 +338,7 @@ def main() -> int:
         bench_step("full", 1)
     ms_full = timed(lambda: bench_step("full", 1), args.steps)
     q_tokens = w.batch * w.block_len * w.steps * len(blocks)
+    gpu_load = snapshot_under_load(lambda: bench_step("full", 1), torch.cuda.synchronize)
 
     # ---- per-step latency: refresh vs reuse steps (first block) ----
     st0 = states[0]
@@ -476,6 +515,8 @@ def main() -> int:
         "drift_per_step": drift,
         "sparse_only_drift_max_abs": max(sparse_only_drift) if sparse_only_drift else None,
         "roofline": roof,
+        "gpu_state": {"idle_before_timing": gpu_idle, "under_full_recompute_steps_after_timing": gpu_load,
+                      "source": "amd-smi metric -g 0 --power --clock"},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")
