@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -441,6 +442,34 @@ fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float
   return hip_status(fb::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, o, lse, stream), "merge launch");
 }
 
+}  // extern "C"
+
+// FB_DEBUG=1 in the environment turns on the reuse-step check below.
+static bool debug_checks() {
+  const char* e = getenv("FB_DEBUG");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+// Debug check before a reuse step: scans the cached partial (O, then LSE)
+// for NaN, with the flag in the first word of the workspace, and waits for
+// the answer on the stream.
+static fb_status cache_has_nan(const fb_desc* d, const float* oc, const float* lc, void* ws, int32_t step,
+                               void* stream) {
+  const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
+  int32_t* flag = (int32_t*)ws;
+  int rc = fb::launch_nan_scan(oc, rows * d->head_dim, flag, true, stream);
+  if (rc == 0) rc = fb::launch_nan_scan(lc, rows, flag, false, stream);
+  int32_t host = 0;
+  if (rc == 0) rc = (int)hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (rc == 0) rc = (int)hipStreamSynchronize((hipStream_t)stream);
+  fb_status st = hip_status(rc, "FB_DEBUG cache check");
+  if (st != FB_OK) return st;
+  if (host) return fail(FB_ERR_ARG, "reuse step %d: the cached partial holds NaN (was it written by a refresh step of this block?)", step);
+  return FB_OK;
+}
+
+extern "C" {
+
 fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
                   const void* v_pre, const fb_sparse* sp, float* o_ext_cache, float* lse_ext_cache,
                   float* o_res_cache, float* lse_res_cache, void* o, float* lse_out, int32_t step,
@@ -469,6 +498,13 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
 
   const bool refresh = mode == FB_MODE_FULL || force_refresh != 0 || step % refresh_period == 0;
   if (refreshed_out) *refreshed_out = refresh ? 1 : 0;
+  if (!refresh && debug_checks()) {
+    // the partial this step reuses: the block-external cache, or the residual in the sparse variant
+    const float* oc = sp ? o_res_cache : o_ext_cache;
+    const float* lc = sp ? lse_res_cache : lse_ext_cache;
+    st = cache_has_nan(d, oc, lc, ws, step, stream);
+    if (st != FB_OK) return st;
+  }
   if (!sp) {
     if (refresh) {
       st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_ALL, nullptr, nullptr, nullptr, o_ext_cache,

@@ -170,5 +170,7 @@ struct SelectArgs {
 int launch_pool(const SelectArgs& a, void* stream);
 int launch_select_pooled(const SelectArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
+// *flag = 1 if any of x[0..n) is NaN (flag cleared first when clear is set)
+int launch_nan_scan(const float* x, int64_t n, int32_t* flag, bool clear, void* stream);
 
 }  // namespace fb

@@ -1424,6 +1424,22 @@ __global__ void __launch_bounds__(1024) topk_kernel(const SelectArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// debug check of a cached partial before a reuse step: *flag = 1 if any value
+// is NaN (every writer stores the same 1, so the race is benign)
+// ---------------------------------------------------------------------------
+
+__global__ void flag_clear_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) *flag = 0;
+}
+
+__global__ void __launch_bounds__(256) nan_scan_kernel(const float* x, int64_t n, int32_t* flag) {
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    bad |= __builtin_isnan(x[i]);
+  if (bad) *flag = 1;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -1512,6 +1528,16 @@ int launch_select_pooled(const SelectArgs& a, void* stream) {
     hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((int64_t)a.B * a.Hkv)), dim3(1024), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+int launch_nan_scan(const float* x, int64_t n, int32_t* flag, bool clear, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (clear) hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+  if (n > 0) {
+    const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(nan_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, flag);
+  }
   return (int)hipGetLastError();
 }
 

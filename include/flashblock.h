@@ -162,7 +162,12 @@ fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float
  *                       partial merged with the residual into (o_ext_cache,
  *                       lse_ext_cache), then the block partial merged into o.
  * A step that does not refresh reads caches written by an earlier refresh step of
- * the same block (same buffers); otherwise its result is undefined.
+ * the same block (same buffers); otherwise its result is undefined.  With the
+ * environment variable FB_DEBUG=1 such a step first scans the cache it reads
+ * (o/lse_ext_cache, or o/lse_res_cache in the sparse variant) for NaN, using the
+ * first word of ws, waits for the answer on the stream, and returns FB_ERR_ARG
+ * before launching anything else if it finds one (a debugging aid: it
+ * synchronises the stream).
  * refreshed_out (host, nullable) receives 1 if this step refreshed.  Full mode
  * recomputes the prefix every step, i.e. the standard per-step attention over the
  * whole KV cache plus the block. */

@@ -1,0 +1,45 @@
+"""FB_DEBUG=1: a reuse step refuses a cache that holds NaN (one no refresh step
+wrote), dense and sparse; without the variable the step runs unchecked."""
+import numpy as np
+import pytest
+import torch
+
+from cached_attention_amd import flashblock as fbl
+from cached_attention_amd import workloads as wl
+from cached_attention_amd.session import AttentionStep
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device="cuda", dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_debug_check_refuses_nan_cache(monkeypatch, sparse):
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=640, hq=8, hkv=2, block_len=16)
+    prefix, blocks = wl.make_inputs(w)
+    blk = blocks[0]
+    chunks = torch.tensor([[[1, 4], [0, 9]]], dtype=torch.int32) if sparse else None
+    st = AttentionStep("bf16", w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets, chunks=chunks)
+    kp, vp = dev(prefix.k), dev(prefix.v)
+    q, k, v = dev(blk.q[1]), dev(blk.k[1]), dev(blk.v[1])
+    monkeypatch.setenv("FB_DEBUG", "1")
+    # step 1 with r = 8 reuses a cache no refresh step wrote: make it NaN
+    cache = st.o_res if sparse else st.o_ext
+    cache.fill_(float("nan"))
+    with pytest.raises(fbl.FlashBlockError) as e:
+        st.step(q, k, v, kp, vp, 1, 8)
+    assert e.value.status == fbl.FB_ERR_ARG
+    assert "NaN" in fbl.fb_last_error()
+    # after a refresh step the same reuse step passes the check and is finite
+    st.step(dev(blk.q[0]), dev(blk.k[0]), dev(blk.v[0]), kp, vp, 0, 8)
+    st.step(q, k, v, kp, vp, 1, 8)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st.o.float()).all()
+    # without the variable nothing is checked: the NaN cache runs through
+    monkeypatch.delenv("FB_DEBUG")
+    cache.fill_(float("nan"))
+    st.step(q, k, v, kp, vp, 1, 8)
+    torch.cuda.synchronize()
+    assert torch.isnan(st.o.float()).any()
