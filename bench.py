@@ -188,7 +188,7 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU (asked for {max(args.gpus, world)}); this build has no "
+        print(f"bench.py measures one GPU (asked for {max(args.gpus, world)}); the library has no "
               f"multi-GPU path", file=sys.stderr)
         return 2
 
