@@ -36,10 +36,11 @@
  *   lse_ext / lse_res / lse_out [B][Hq][Lb] contiguous fp32.
  *
  * Ownership.  The caller allocates and owns every buffer (inputs, outputs,
- * caches, workspace, device offsets).  The library never allocates, frees or
- * synchronises device memory and keeps no state between calls.  All device
- * work is enqueued asynchronously on the caller's stream (`stream` is a
- * hipStream_t passed as void*; NULL is the null stream).
+ * caches, workspace, device offsets).  The library never allocates or frees
+ * device memory and keeps no state between calls.  All device work is
+ * enqueued asynchronously on the caller's stream (`stream` is a hipStream_t
+ * passed as void*; NULL is the null stream); nothing synchronises except the
+ * opt-in FB_DEBUG check of fb_step.
  *
  * Errors.  Arguments are validated before anything is enqueued: on an error
  * nothing is launched, outputs are untouched, the status code says which check
@@ -106,8 +107,9 @@ typedef struct fb_sparse {
 } fb_sparse;
 
 /* Bytes of workspace fb_prefix_attn / fb_step / fb_step_masked /
- * fb_refresh_mask_tau need for this shape (split-KV partials, tau flags).  `sp` may be NULL (dense prefix).  For fb_step in sparse mode pass
- * the fb_sparse it will get; the larger of the SELECTED and COMPLEMENT plans is
+ * fb_refresh_mask_tau need for this shape (split-KV partials, tau flags).
+ * `sp` may be NULL (dense prefix).  For fb_step in sparse mode pass the
+ * fb_sparse it will get; the larger of the SELECTED and COMPLEMENT plans is
  * returned.  Returns 0 on invalid arguments (see fb_last_error()). */
 size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp);
 
@@ -253,7 +255,8 @@ fb_status fb_select_chunks(const fb_desc* d, const void* q_blk, const void* k_pr
  * chunks untouched: after appending a block, first_chunk = the smallest old
  * stream length / chunk_len (rounded down) re-pools the partial last chunk
  * and pools the new ones.  fb_select_chunks_pooled scores and selects from
- * pooled; scores is caller-owned fp32 [B][Hkv][chunk_cap] scratch. */
+ * pooled; scores is caller-owned fp32 [B][Hkv][chunk_cap] scratch.  A
+ * chunk_cap below the longest stream's chunk count is FB_ERR_ARG. */
 fb_status fb_pool_chunk_keys(const fb_desc* d, const void* k_pre, int32_t chunk_len, int32_t chunk_cap,
                              int32_t first_chunk, float* pooled, void* stream);
 fb_status fb_select_chunks_pooled(const fb_desc* d, const void* q_blk, const float* pooled, int32_t chunk_len,
