@@ -127,6 +127,33 @@ def test_text_gqa_sparse(r):
     check_block(w, prefix, blocks[0], r, "cached", chunks=chunks)
 
 
+@pytest.mark.parametrize("r", [1, 2])
+def test_sparse_chunk128_ragged_batch(r):
+    """128-token chunks (two 64-key tiles each) over two ragged streams whose
+    last chunks are partial; GQA 8/2, block 16."""
+    w = wl.Workload("sp128", "bf16", 2, 8, 2, 128, 16, 1500, 3, 0.5, 0.05, ragged=0.3, seed=91,
+                    sparse_keep=0.25, chunk_len=128)
+    prefix, blocks = wl.make_inputs(w)
+    chunks = wl.make_chunk_selection(w, prefix.lengths)
+    assert chunks.shape[-1] >= 2 and all(l % 128 for l in prefix.lengths)
+    for b in range(w.batch):   # include each stream's partial last chunk
+        last = (prefix.lengths[b] - 1) // 128
+        for g in range(w.hkv):
+            if last not in chunks[b, g]:
+                chunks[b, g, -1] = last
+                chunks[b, g] = np.sort(chunks[b, g])
+    scale = scale_of(w)
+    ref = oracle.run_block(prefix.k, prefix.v, prefix.offsets, blocks[0].q, blocks[0].k, blocks[0].v, scale, r=r,
+                           chunks=chunks, chunk_len=128)
+    st = AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets,
+                       chunks=torch.from_numpy(chunks), chunk_len=128)
+    got = run_gpu(w, prefix, blocks[0], r, "cached", st=st)
+    for s in range(w.steps):
+        err = np.abs(got.out[s] - ref.out[s]).max()
+        assert err <= 2e-2, f"step {s}: max|O - O_ref| = {err:.3e}"
+        assert np.abs(got.lse[s] - ref.lse[s]).max() <= 2e-2
+
+
 @pytest.mark.parametrize("r,mode", [(1, "cached"), (4, "cached"), (1, "full")])
 def test_video_frame_block(r, mode):
     w = wl.ci_version(wl.WORKLOADS["video_1560"], prefix_len=3120, hq=4, hkv=4, n_blocks=1)
