@@ -93,8 +93,8 @@ def test_tau_mask_counts_exact(dtype):
     assert seen == {0, 1}   # the threshold both reuses and recomputes in this block
 
 
-def _gamma_case():
-    w, p, blk = _setup("bf16", 1, 6, 6, 128, 100, 200, 5, 0.1, seed=43, head_spread=0.9, reveal=False)
+def _gamma_case(dtype="bf16"):
+    w, p, blk = _setup(dtype, 1, 6, 6, 128, 100, 200, 5, 0.1, seed=43, head_spread=0.9, reveal=False)
     gamma = 0.993
     ref = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, 1 / math.sqrt(w.head_dim),
                                   "gamma", gamma=gamma)
@@ -105,8 +105,9 @@ def _gamma_case():
     return w, p, blk, gamma, ref
 
 
-def test_gamma_mask_and_reference_queries():
-    w, p, blk, gamma, ref = _gamma_case()
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gamma_mask_and_reference_queries(dtype):
+    w, p, blk, gamma, ref = _gamma_case(dtype)
     g = Gpu(w, p, blk)
     q_ref = None
     for s in range(w.steps):
