@@ -160,8 +160,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="text_mha_32k")
     ap.add_argument("--r", type=int, default=8)
-    ap.add_argument("--kv-layout", choices=("head", "token"), default="head",
-                    help="prefix KV cache layout: head-major [Hkv][T][D] or token-major [T][Hkv][D]")
+    ap.add_argument("--kv-layout", choices=("head", "token", "interleave"), default="head",
+                    help="prefix KV cache layout: head-major [Hkv][T][D], token-major [T][Hkv][D], or head-major "
+                         "with each token's K and V rows adjacent [Hkv][T][2][D]")
     ap.add_argument("--sparse", action="store_true",
                     help="chunk-sparse variant: cached residual of the unselected 64-token chunks plus a fresh "
                          "partial over the selected ones (workloads with a sparse keep fraction)")
@@ -258,11 +259,21 @@ def main() -> int:
     head_major = args.kv_layout == "head"
     # head-major keeps each KV head's keys contiguous: a 64-key tile is one 16 KB run
     dev_kv = (lambda x: dev(np.transpose(x, (1, 0, 2)))) if head_major else dev
+
+    def interleaved(kp, vp):
+        """[Hkv][T][2][D]: each token's K and V rows adjacent; K and V are strided views."""
+        il = dev(np.stack([np.transpose(kp, (1, 0, 2)), np.transpose(vp, (1, 0, 2))], axis=2))
+        return il[:, :, 0, :], il[:, :, 1, :]
+
     layers = []   # N_LAYERS copies of each block's prefix
     pre_strides = []
     for j in range(len(blocks)):
         kp, vp, _ = block_prefix[j]
         t_tot = kp.shape[0]
+        if args.kv_layout == "interleave":
+            pre_strides.append((2 * w.head_dim, 2 * t_tot * w.head_dim))
+            layers.append([interleaved(kp, vp) for _ in range(N_LAYERS)])
+            continue
         pre_strides.append((w.head_dim, t_tot * w.head_dim) if head_major else (w.hkv * w.head_dim, w.head_dim))
         k0, v0 = dev_kv(kp), dev_kv(vp)
         layers.append([(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(N_LAYERS - 1)])
@@ -486,7 +497,8 @@ def main() -> int:
             "workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "head_dim": w.head_dim,
             "block_len": w.block_len, "prefix_len": lens if w.batch > 1 else lens[0],
             "denoise_steps": w.steps, "blocks": len(blocks), "refresh_period": r,
-            "kv_layout": "head-major [Hkv][T][D]" if head_major else "token-major [T][Hkv][D]",
+            "kv_layout": {"head": "head-major [Hkv][T][D]", "token": "token-major [T][Hkv][D]",
+                          "interleave": "per-token K/V interleave [Hkv][T][2][D]"}[args.kv_layout],
             "sparse": ({"chunks_kept": k_sel, "chunk_len": 64, "residual": "cached at refresh steps",
                         "selection": ("top-k on the GPU at each block's first step (inside the step); pooled "
                                       "chunk keys kept per layer, the block's new chunks pooled in the step" if topk
