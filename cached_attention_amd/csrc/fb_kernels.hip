@@ -14,6 +14,15 @@
 //              equation generalised to n partials), optionally folding in one
 //              more partial (the sparse variant's cached residual).
 // merge      -- the merge equation on two fp32 partials.
+// tau_flags / tau_finalize, gamma
+//            -- the adaptive reuse decisions: updated-token counts and
+//              per-head query similarities, turned into recompute masks.
+// append     -- the finalised block's K/V rows into the prefix cache.
+// pool / score / topk
+//            -- chunk selection for the sparse variant: mean-pooled chunk
+//              keys, max query score per chunk, top-k by radix select.
+// flag_clear / nan_scan
+//            -- the opt-in debug check of a cache before a reuse step.
 //
 // Layout of one bf16 LDS stage (64 keys, head_dim D):
 //   K tile  [64 keys][D]   row = 2D bytes, 16-byte slot c of key t stored at
