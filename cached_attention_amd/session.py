@@ -17,6 +17,18 @@ _DT = {"bf16": (fbl.FB_BF16, torch.bfloat16), "f32": (fbl.FB_F32, torch.float32)
 
 
 class AttentionStep:
+    """Caches, workspace and outputs of one attention layer shape.
+
+    dtype "bf16" or "f32"; ``prefix_offsets`` int [B+1] (stream b owns prefix
+    rows off[b] .. off[b+1]-1); ``pre_strides`` (token stride, head stride) in
+    elements of the prefix K/V, default token-major [T][Hkv][D].  With
+    ``chunks`` (int32 [B][Hkv][k], ascending) the sparse variant runs: the
+    residual of the unselected ``chunk_len``-token chunks is cached at refresh
+    steps.  After a step, ``o`` [B][Lb][Hq][D] holds the output, ``lse``
+    [B][Hq][Lb] its natural-log LSE, ``o_ext`` / ``lse_ext`` the block-external
+    partial used (fp32).
+    """
+
     def __init__(self, dtype: str, batch: int, hq: int, hkv: int, head_dim: int, block_len: int,
                  prefix_offsets: Sequence[int], device="cuda", chunks: Optional[torch.Tensor] = None,
                  chunk_len: int = 64, softmax_scale: float = 0.0, pre_strides=None):
@@ -45,6 +57,12 @@ class AttentionStep:
 
     def step(self, q, k, v, k_pre, v_pre, step: int, refresh_period: int = 1, mode: str = "cached",
              force_refresh: bool = False, want_lse: bool = True, stream=None) -> bool:
+        """One denoising step through fb_step; returns whether it refreshed the cache.
+
+        q [B][Lb][Hq][D], k / v [B][Lb][Hkv][D] (contiguous, this shape's dtype);
+        ``step`` counts from 0 within the block; mode "cached" refreshes when
+        step % refresh_period == 0 (or on ``force_refresh``), "full" every step.
+        """
         m = fbl.FB_MODE_FULL if mode == "full" else fbl.FB_MODE_CACHED
         return fbl.fb_step(self.desc, q, k, v, k_pre, v_pre, self.sparse, self.o_ext, self.lse_ext,
                            self.o_res, self.lse_res, self.o, self.lse if want_lse else None, step,
