@@ -450,6 +450,13 @@ static bool debug_checks() {
   return e && e[0] == '1' && e[1] == '\0';
 }
 
+// The debug check waits on the stream, which a stream under graph capture
+// cannot do: it is skipped there.
+static bool capturing(void* stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing((hipStream_t)stream, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 // Debug check before a reuse step: scans the cached partial (O, then LSE)
 // for NaN, with the flag in the first word of the workspace, and waits for
 // the answer on the stream.
@@ -498,7 +505,7 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
 
   const bool refresh = mode == FB_MODE_FULL || force_refresh != 0 || step % refresh_period == 0;
   if (refreshed_out) *refreshed_out = refresh ? 1 : 0;
-  if (!refresh && debug_checks()) {
+  if (!refresh && debug_checks() && !capturing(stream)) {
     // the partial this step reuses: the block-external cache, or the residual in the sparse variant
     const float* oc = sp ? o_res_cache : o_ext_cache;
     const float* lc = sp ? lse_res_cache : lse_ext_cache;

@@ -169,7 +169,8 @@ fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float
  * (o/lse_ext_cache, or o/lse_res_cache in the sparse variant) for NaN, using the
  * first word of ws, waits for the answer on the stream, and returns FB_ERR_ARG
  * before launching anything else if it finds one (a debugging aid: it
- * synchronises the stream).
+ * synchronises the stream, so it is skipped while the stream is being
+ * captured into a graph).
  * refreshed_out (host, nullable) receives 1 if this step refreshed.  Full mode
  * recomputes the prefix every step, i.e. the standard per-step attention over the
  * whole KV cache plus the block. */

@@ -43,3 +43,28 @@ def test_debug_check_refuses_nan_cache(monkeypatch, sparse):
     st.step(q, k, v, kp, vp, 1, 8)
     torch.cuda.synchronize()
     assert torch.isnan(st.o.float()).any()
+
+
+def test_debug_check_is_skipped_under_graph_capture(monkeypatch):
+    """The check synchronises, which a capturing stream cannot: with FB_DEBUG=1
+    a reuse step still captures, and its replay matches the eager step."""
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=640, hq=8, hkv=2, block_len=16)
+    prefix, blocks = wl.make_inputs(w)
+    blk = blocks[0]
+    st = AttentionStep("bf16", w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets)
+    kp, vp = dev(prefix.k), dev(prefix.v)
+    q, k, v = dev(blk.q[1]), dev(blk.k[1]), dev(blk.v[1])
+    monkeypatch.setenv("FB_DEBUG", "1")
+    st.step(dev(blk.q[0]), dev(blk.k[0]), dev(blk.v[0]), kp, vp, 0, 8)
+    st.step(q, k, v, kp, vp, 1, 8)
+    torch.cuda.synchronize()
+    ref = st.o.clone()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            st.step(q, k, v, kp, vp, 1, 8, stream=torch.cuda.current_stream())
+    st.o.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(st.o, ref)
