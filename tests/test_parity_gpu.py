@@ -127,6 +127,15 @@ def test_text_gqa_sparse(r):
     check_block(w, prefix, blocks[0], r, "cached", chunks=chunks)
 
 
+@pytest.mark.parametrize("hq,hkv,lb,mode", [(2, 2, 1100, "cached"), (8, 2, 300, "cached"), (8, 2, 300, "full")])
+def test_big_block_ragged_streams(hq, hkv, lb, mode):
+    """Blocks of >= 1024 query rows per KV head (the 8-wave block configuration),
+    MHA and GQA, over two ragged streams, cached and full."""
+    w = wl.Workload("big", "bf16", 2, hq, hkv, 128, lb, 300, 3, 1.0, 0.1, ragged=0.25, seed=97)
+    prefix, blocks = wl.make_inputs(w)
+    check_block(w, prefix, blocks[0], 2, mode)
+
+
 @pytest.mark.parametrize("r", [1, 2])
 def test_sparse_chunk128_ragged_batch(r):
     """128-token chunks (two 64-key tiles each) over two ragged streams whose
