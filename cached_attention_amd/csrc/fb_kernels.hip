@@ -298,6 +298,15 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* s
 #endif
 constexpr int kVAhead = FB_V_AHEAD;   // V^T fragment groups read ahead of their MFMAs
 constexpr int kKAhead = FB_K_AHEAD;   // K fragment k-steps read ahead of their MFMAs
+#ifndef FB_PV_DEFER
+#define FB_PV_DEFER 2
+#endif
+// PV MFMA groups of a tile deferred to the start of the next tile, where they
+// run while that tile's first K fragments are read from LDS (the same
+// accumulation order, so bitwise the same result).  Measured on MI355X: 2
+// groups take 2.7% off the 128K GQA prefix pass and 1.5% off the video one;
+// 4 or 6 gain nothing.
+constexpr int kPvDefer = FB_PV_DEFER;
 #ifndef FB_MFMA_PRIO
 #define FB_MFMA_PRIO 1
 #endif
@@ -445,13 +454,29 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   const int vkx = kv_swz<D>(4 * lg + (l16 >> 2)) >> 1;
 
   f32x4 s[4][QT];
+  // V^T fragments of the deferred PV groups; their P^T operands stay in pf
+  bf16x8 vdef[kPvDefer > 0 ? kPvDefer : 1];
+  bf16x8 pf[2][QT];
+  auto run_deferred = [&]() __attribute__((always_inline)) {
+    if constexpr (kPvDefer > 0) {
+      mfma_prio<1>();
+#pragma unroll
+      for (int d = 0; d < kPvDefer; ++d) {
+        const int g = NG - kPvDefer + d;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[g % DT][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vdef[d], pf[g / DT][qt], oacc[g % DT][qt], 0, 0, 0);
+      }
+      mfma_prio<0>();
+    }
+  };
 
   // S^T = K Q^T for the tile at LDS offset kb; k-step outer so that the
   // 4 x QT accumulators of a step are independent MFMA chains.  The K
   // fragments of step ks+1 are read while the MFMAs of step ks run; the
   // scheduling fences keep the compiler from sinking the reads next to
   // their MFMAs, where each group would wait out the LDS latency.
-  auto scores = [&](uint32_t kb) __attribute__((always_inline)) {
+  auto scores = [&](uint32_t kb, auto pend_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -464,6 +489,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     };
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks) kload(ks);
+    if constexpr (decltype(pend_tag)::value != 0) {   // the previous tile's last PV groups cover the K reads
+      __builtin_amdgcn_sched_barrier(0);
+      run_deferred();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mfma_prio<1>();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -493,7 +523,6 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // p = exp2(s*c - m) against the reference, packed to bf16 for the PV
   // product; the packed values (this lane's 16 keys of each row) are summed
   // into l with v_dot2 against (1, 1)
-  bf16x8 pf[2][QT];
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones2 = {(__bf16)1.f, (__bf16)1.f};
   auto exps = [&]() __attribute__((always_inline)) {
@@ -574,9 +603,13 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     for (int g = 0; g < NG; ++g) {
       if (g + kVAhead < NG) vload(g + kVAhead);
       __builtin_amdgcn_sched_barrier(0);
+      if (g >= NG - kPvDefer) {
+        vdef[g - (NG - kPvDefer)] = vf[g];   // runs at the start of the next tile (or the pass's end)
+      } else {
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        oacc[g % DT][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g], pf[g / DT][qt], oacc[g % DT][qt], 0, 0, 0);
+        for (int qt = 0; qt < QT; ++qt)
+          oacc[g % DT][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[g], pf[g / DT][qt], oacc[g % DT][qt], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_prio<0>();
@@ -590,7 +623,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // one tile: wait for it (tiles issued after it may stay in flight), one
   // barrier (every wave is done with the stage refilled next), issue the tile
   // DIST ahead, compute, advance the queue
-  auto tile_step = [&](auto mode_tag) __attribute__((always_inline)) {
+  auto tile_step = [&](auto mode_tag, auto pend_tag) __attribute__((always_inline)) {
     int after = 0;
 #pragma unroll
     for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
@@ -600,7 +633,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
     const uint32_t kb = lds0 + st * STAGE;
     if (wave_active) {
-      scores(kb);
+      scores(kb, pend_tag);
       softmax_pv(kb + TBYTES, q_nv[0], mode_tag);
     }
 #pragma unroll
@@ -622,8 +655,14 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
     }
     if (!q_have[0]) return false;
-    tile_step(first_tag);
-    while (q_have[0]) tile_step(rest_tag);
+    // PV groups deferred by a tile run at the start of the next tile of the
+    // same pass, and at the pass's end (scores-only passes defer nothing)
+    constexpr bool defer = kPvDefer > 0 && decltype(rest_tag)::value != 2;
+    tile_step(first_tag, IC<0>{});
+    while (q_have[0]) tile_step(rest_tag, IC<defer ? 1 : 0>{});
+    if constexpr (defer) {
+      if (wave_active) run_deferred();
+    }
     return true;
   };
   const TileIter it0 = wk.it;
