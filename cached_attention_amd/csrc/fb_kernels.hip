@@ -476,19 +476,22 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // fragments of step ks+1 are read while the MFMAs of step ks run; the
   // scheduling fences keep the compiler from sinking the reads next to
   // their MFMAs, where each group would wait out the LDS latency.
+  bf16x8 kf[KS][4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
+  auto kload = [&](uint32_t kb, int ks) __attribute__((always_inline)) {
+    const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
+  };
+  // the first K reads of a tile, issued as early as possible after its barrier
+  auto scores_begin = [&](uint32_t kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < kKAhead; ++ks) kload(kb, ks);
+  };
   auto scores = [&](uint32_t kb, auto pend_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[KS][4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
-    auto kload = [&](int ks) __attribute__((always_inline)) {
-      const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
-    };
-#pragma unroll
-    for (int ks = 0; ks < kKAhead; ++ks) kload(ks);
     if constexpr (decltype(pend_tag)::value != 0) {   // the previous tile's last PV groups cover the K reads
       __builtin_amdgcn_sched_barrier(0);
       run_deferred();
@@ -497,7 +500,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     mfma_prio<1>();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks + kKAhead < KS) kload(ks + kKAhead);
+      if (ks + kKAhead < KS) kload(kb, ks + kKAhead);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
@@ -629,9 +632,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
     wait_vmcnt_tiles<IPW>(after);
     lds_dma_barrier();
+    const uint32_t kb = lds0 + st * STAGE;
+    if (wave_active) scores_begin(kb);   // stage st is read, stage st + DIST filled: independent
     q_have[DIST] = q_have[DIST - 1] && next_tile(wk.it, q_tok[DIST], q_nv[DIST]);
     if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
-    const uint32_t kb = lds0 + st * STAGE;
     if (wave_active) {
       scores(kb, pend_tag);
       softmax_pv(kb + TBYTES, q_nv[0], mode_tag);
