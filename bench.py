@@ -125,18 +125,29 @@ def blas_threads() -> int:
     return 1
 
 
-def cpu_baseline(w, prefix, blocks, r, budget_s=15.0):
-    """The fp64 oracle (as it stands) on the same workload's first block in
-    cached mode, on the host cores; repeated until ~budget_s of CPU work."""
+def cpu_baseline(w, prefix, blocks, r, budget_s=15.0, variant="fixed", k_sel=0, tau=0, eps=0.0, gamma=0.0):
+    """The fp64 oracle (as it stands) on the same workload's first block, in
+    the variant the GPU runs (fixed-period cached, sparse with the oracle's own
+    chunk selection at the block's first step, or an adaptive reuse policy), on
+    the host cores; repeated until ~budget_s of CPU work."""
     import oracle
     scale = 1.0 / math.sqrt(w.head_dim)
     blk = blocks[0]
-    # bound the sample: whole streams and query heads of one block, cut down to
-    # fit the budget; the rate is per query token, so it scales linearly
+
+    def one_block():
+        if variant == "sparse":
+            chunks = oracle.select_chunks(blk.q[0], prefix.k, prefix.offsets, k_sel, 64)
+            oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r, chunks=chunks)
+        elif variant in ("tau", "gamma"):
+            oracle.run_block_policy(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, variant,
+                                    tau=tau, eps=eps, gamma=gamma)
+        else:
+            oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r)
+
     t0 = time.perf_counter()
     runs = 0
     while True:
-        oracle.run_block(prefix.k, prefix.v, prefix.offsets, blk.q, blk.k, blk.v, scale, r=r)
+        one_block()
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 100:
@@ -148,7 +159,7 @@ def cpu_baseline(w, prefix, blocks, r, budget_s=15.0):
         "unit": "query-tok/s",
         "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"{runs} x first block of {w.name} ({w.steps} steps, r={r}, all streams and heads), "
+        "sample": f"{runs} x first block of {w.name} ({w.steps} steps, {variant}, r={r}, all streams and heads), "
                   f"numpy fp64, {el:.1f} s; BLAS threads as cores, elementwise single-threaded",
     }
 
@@ -532,7 +543,9 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")
-        result["cpu_baseline"] = cpu_baseline(w, wl.Prefix(*block_prefix[0]), blocks, r)
+        variant = "sparse" if args.sparse else args.policy
+        result["cpu_baseline"] = cpu_baseline(w, wl.Prefix(*block_prefix[0]), blocks, r, variant=variant,
+                                              k_sel=k_sel, tau=args.tau, eps=args.eps, gamma=args.gamma)
     print(json.dumps(result), flush=True)
     return 0
 

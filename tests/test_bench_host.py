@@ -72,3 +72,14 @@ def test_bench_measures_one_gpu_only():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_runs_the_gpu_variant():
+    """The oracle baseline times the same variant as the GPU run: fixed period,
+    sparse with its own chunk selection, or an adaptive reuse policy."""
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=640, hq=8, hkv=2, block_len=16)
+    prefix, blocks = wl.make_inputs(w)
+    for variant, kw in [("fixed", {}), ("sparse", {"k_sel": 2}), ("tau", {"tau": 4, "eps": 0.25}),
+                        ("gamma", {"gamma": 0.99})]:
+        r = bench.cpu_baseline(w, prefix, blocks, 2, budget_s=0.05, variant=variant, **kw)
+        assert r["value"] > 0 and r["kind"] == "oracle" and f", {variant}, " in r["sample"]
