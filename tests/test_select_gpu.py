@@ -49,9 +49,10 @@ def _select_gpu(w, prefix, q, k, head_major=False):
     return idx.cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype,head_major", [("bf16", False), ("bf16", True), ("f32", False)])
-def test_select_chunks_matches_oracle(dtype, head_major):
-    w = wl.Workload("sel", dtype, 2, 8, 2, 128, 16, 2000, 2, 1.0, 0.1, ragged=0.25, seed=71)
+@pytest.mark.parametrize("dtype,head_major,d", [("bf16", False, 128), ("bf16", True, 128), ("f32", False, 128),
+                                               ("bf16", True, 64), ("f32", False, 64)])
+def test_select_chunks_matches_oracle(dtype, head_major, d):
+    w = wl.Workload("sel", dtype, 2, 8, 2, d, 16, 2000, 2, 1.0, 0.1, ragged=0.25, seed=71)
     prefix, blocks = wl.make_inputs(w)
     q = blocks[0].q[0]
     k = 4
