@@ -76,9 +76,9 @@ class Gpu:
                            self.lse_ext, self.o, self.lse, self.ws, self.ws_bytes)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_tau_mask_counts_exact(dtype):
-    w, p, blk = _setup(dtype, 2, 8, 2, 128, 40, 300, 6, 0.05, seed=41)
+@pytest.mark.parametrize("dtype,d,seed", [("bf16", 128, 41), ("f32", 128, 41), ("bf16", 64, 42)])
+def test_tau_mask_counts_exact(dtype, d, seed):
+    w, p, blk = _setup(dtype, 2, 8, 2, d, 40, 300, 6, 0.05, seed=seed)
     g = Gpu(w, p, blk)
     eps, tau = 0.5, 7
     ref = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, 1 / math.sqrt(w.head_dim),
@@ -125,9 +125,9 @@ def test_gamma_mask_and_reference_queries(dtype):
         np.testing.assert_array_equal(g.q_ref.float().cpu().numpy(), q_ref)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_step_masked_tau_policy(dtype):
-    w, p, blk = _setup(dtype, 2, 8, 2, 128, 40, 300, 6, 0.05, seed=47)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("f32", 64)])
+def test_step_masked_tau_policy(dtype, d):
+    w, p, blk = _setup(dtype, 2, 8, 2, d, 40, 300, 6, 0.05, seed=47)
     g = Gpu(w, p, blk)
     eps, tau = 0.5, 7
     ref = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, 1 / math.sqrt(w.head_dim),
