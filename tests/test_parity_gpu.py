@@ -277,6 +277,45 @@ def test_drift_parity():
             assert d_gpu == 0.0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partials_then_combine_with_extra_partial(dtype):
+    """fb_prefix_partials + fb_prefix_combine called on their own, the combine
+    folding in one more partial: equals the oracle's prefix partial merged with
+    that partial by the merge equation (and, without it, fb_prefix_attn)."""
+    w = wl.Workload("pc", dtype, 2, 8, 2, 128, 16, 700, 1, 1.0, 0.1, ragged=0.3, seed=101)
+    prefix, blocks = wl.make_inputs(w)
+    q = blocks[0].q[0]
+    t = TDT[dtype]
+    off_dev = torch.tensor(prefix.offsets, dtype=torch.int64, device="cuda")
+    desc = fbl.Desc(fbl.FB_BF16 if dtype == "bf16" else fbl.FB_F32, w.batch, w.hq, w.hkv, w.head_dim, w.block_len,
+                    prefix.offsets, off_dev)
+    wsb = fbl.fb_workspace_size(desc)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(5)
+    xo = rng.standard_normal((w.batch, w.hq, w.block_len, w.head_dim))
+    xl = rng.standard_normal((w.batch, w.hq, w.block_len)) * 3
+    xl[0, 0, :3] = -np.inf          # a few rows with an empty extra partial
+    xo[0, 0, :3] = 0.0
+    fx = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    oe = torch.empty(w.batch, w.hq, w.block_len, w.head_dim, device="cuda")
+    le = torch.empty(w.batch, w.hq, w.block_len, device="cuda")
+    fbl.fb_prefix_partials(desc, dev(q, t), dev(prefix.k, t), dev(prefix.v, t), None, ws, wsb)
+    fbl.fb_prefix_combine(desc, None, fx(xo), fx(xl), oe, le, ws, wsb)
+    torch.cuda.synchronize()
+    po, pl = oracle.prefix_partial(q, prefix.k, prefix.v, prefix.offsets, scale_of(w))
+    ro, rl = oracle.merge(po, pl, xo.astype(np.float32).astype(np.float64), xl.astype(np.float32).astype(np.float64))
+    tl = 2e-2 if dtype == "bf16" else 1e-5 * max(1.0, float(np.abs(ro).max()))
+    assert np.abs(oe.cpu().numpy() - ro).max() <= tl
+    assert np.abs(le.cpu().numpy() - rl).max() <= (2e-2 if dtype == "bf16" else 1e-5 * max(1.0, np.abs(rl).max()))
+    # without the extra partial the combine equals fb_prefix_attn
+    fbl.fb_prefix_combine(desc, None, None, None, oe, le, ws, wsb)
+    o2 = torch.empty_like(oe)
+    l2 = torch.empty_like(le)
+    fbl.fb_prefix_attn(desc, dev(q, t), dev(prefix.k, t), dev(prefix.v, t), None, o2, l2, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(oe, o2) and torch.equal(le, l2)
+
+
 def test_fb_merge_matches_oracle():
     rng = np.random.default_rng(5)
     rows, d = 1000, 128
