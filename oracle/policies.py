@@ -25,6 +25,9 @@ Readings of what the page leaves open (plainest choices):
 
 Masks are int arrays [B][Hkv]: 1 = recompute the block-external partial of
 this (stream, KV head) at this step, 0 = reuse the cached one.
+
+The module also holds the chunk selection of the sparse variant (pooled chunk
+keys, max query score, top-k; its own section below, with its readings).
 """
 from __future__ import annotations
 
