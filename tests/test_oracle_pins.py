@@ -467,6 +467,43 @@ def test_gamma_mask_groups_and_threshold():
     assert oracle.gamma_mask(sim, 0.0, 0, 4, 2).tolist() == [[1, 1], [1, 1]]
 
 
+def test_gamma_reference_moves_only_on_recompute():
+    """The head's reference queries are those of its last recompute.
+
+    Each head's queries rotate in a fixed plane: q(t) = cos t x + sin t y with
+    x, y orthonormal over the flattened (position, dim) vector, so the cosine
+    similarity of two steps is the cosine of their angle difference.
+    Head 0 turns 60 degrees then stays: 0.5 (recompute), then 1 against the new
+    reference (reuse).  Head 1 turns by t with cos t = 0.95 twice: 0.95 (reuse,
+    the reference stays at step 0), then cos 2t = 0.805 (recompute).  With
+    gamma 0.9 the masks are [1, 0] then [0, 1].
+    """
+    w, p, blk = _decoding_block(steps=3, hq=2, hkv=2)
+    scale = 1 / math.sqrt(w.head_dim)
+    rng = np.random.default_rng(5)
+    n = w.block_len * w.head_dim
+    basis, _ = np.linalg.qr(_rand(rng, n, 4))
+    t1 = math.acos(0.95)
+    angles = {0: [0.0, math.pi / 3, math.pi / 3], 1: [0.0, t1, 2 * t1]}
+    q_steps = []
+    for s in range(3):
+        q = np.zeros((w.batch, w.block_len, 2, w.head_dim))
+        for h in (0, 1):
+            x, y = basis[:, 2 * h], basis[:, 2 * h + 1]
+            v = math.cos(angles[h][s]) * x + math.sin(angles[h][s]) * y
+            q[:, :, h, :] = v.reshape(w.block_len, w.head_dim)
+        q_steps.append(q)
+    res = oracle.run_block_policy(p.k, p.v, p.offsets, q_steps, blk.k, blk.v, scale, "gamma", gamma=0.9)
+    np.testing.assert_allclose(res.sims[1], [[0.5, 0.95]] * w.batch, atol=1e-12)
+    np.testing.assert_allclose(res.sims[2], [[1.0, 2 * 0.95 ** 2 - 1]] * w.batch, atol=1e-12)
+    assert res.masks[1].tolist() == [[1, 0]] * w.batch
+    assert res.masks[2].tolist() == [[0, 1]] * w.batch
+    # the kept partial is the one of the step that last recomputed the head
+    np.testing.assert_array_equal(res.o_ext[2][:, 0], res.o_ext[1][:, 0])
+    np.testing.assert_array_equal(res.o_ext[1][:, 1], res.o_ext[0][:, 1])
+    assert not np.array_equal(res.o_ext[2][:, 1], res.o_ext[1][:, 1])
+
+
 def _decoding_block(seed=31, steps=5, lp=130, hq=4, hkv=2, head_spread=0.0):
     w = wl.Workload("p", "f32", 2, hq, hkv, 16, 12, lp, steps, 1.0, 0.05, ragged=0.25, seed=seed)
     rng = np.random.default_rng(seed)
