@@ -44,18 +44,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+LIBRARY_SOURCES = ("fb_kernels.hip", "fb_api.cpp", "fb_internal.h")
+
+
+def library_source_sha(root=None):
+    """First 16 hex digits of the sha256 over the library's sources: the kernels,
+    and the host planner and shared header that pick each pass's configuration.
+    None if one is missing."""
+    here = root or os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for name in LIBRARY_SOURCES:
+        path = os.path.join(here, "cached_attention_amd", "csrc", name)
+        if not os.path.exists(path):
+            return None
+        h.update(name.encode() + b"\0" + open(path, "rb").read() + b"\0")
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the prefix kernel from profiles/hbm_traffic.md, or None.
 
-    The table records the sha256 of the kernel source the counters were taken
-    with; a row only counts while the source still hashes the same.
+    The table records the hash of the library sources the counters were taken
+    with (library_source_sha); a row only counts while they still hash the same.
     """
     here = os.path.dirname(os.path.abspath(__file__))
     table = os.path.join(here, "profiles", "hbm_traffic.md")
-    src = os.path.join(here, "cached_attention_amd", "csrc", "fb_kernels.hip")
-    if not (os.path.exists(table) and os.path.exists(src)):
+    sha = library_source_sha(here)
+    if not os.path.exists(table) or sha is None:
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     for line in open(table):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(cells) == 6 and cells[0] == workload and cells[1] == sha:
@@ -194,6 +210,9 @@ def main() -> int:
     ap.add_argument("--prefix-len", type=int, default=0,
                     help="override the workload's prefix length (tokens per stream), e.g. a 128K -> 800K sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip the amd-smi power and clock snapshots (and the extra full-recompute steps "
+                         "that run under the second one), e.g. under a profiler")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale FETCH_SIZE / WRITE_SIZE "
                          "counters) and exit")
@@ -351,7 +370,7 @@ def main() -> int:
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n   # ms
 
-    gpu_idle = smi_snapshot()
+    gpu_idle = None if args.no_gpu_state else smi_snapshot()
     # ---- whole bench steps: cached (r) and full recompute ----
     for _ in range(args.warmup):
         bench_step("cached", r)
@@ -360,7 +379,8 @@ def main() -> int:
         bench_step("full", 1)
     ms_full = timed(lambda: bench_step("full", 1), args.steps)
     q_tokens = w.batch * w.block_len * w.steps * len(blocks)
-    gpu_load = snapshot_under_load(lambda: bench_step("full", 1), torch.cuda.synchronize)
+    gpu_load = (None if args.no_gpu_state
+                else snapshot_under_load(lambda: bench_step("full", 1), torch.cuda.synchronize))
 
     # ---- per-step latency: refresh vs reuse steps (first block) ----
     st0 = states[0]
@@ -538,8 +558,9 @@ def main() -> int:
         "drift_per_step": drift,
         "sparse_only_drift_max_abs": max(sparse_only_drift) if sparse_only_drift else None,
         "roofline": roof,
-        "gpu_state": {"idle_before_timing": gpu_idle, "under_full_recompute_steps_after_timing": gpu_load,
-                      "source": "amd-smi metric -g 0 --power --clock"},
+        "gpu_state": (None if args.no_gpu_state else
+                      {"idle_before_timing": gpu_idle, "under_full_recompute_steps_after_timing": gpu_load,
+                       "source": "amd-smi metric -g 0 --power --clock"}),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host ...")

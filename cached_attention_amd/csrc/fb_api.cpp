@@ -53,8 +53,11 @@ int prefix_cfg(const fb_desc* d) {
 #else
   // measured on MI355X: two independent workgroups per CU, each 2-stage
   // (their waves drift apart, so one's softmax overlaps the other's MFMAs);
-  // 256-row KV heads take two 128-row tiles that share K/V through L2
-  return rows <= 32 ? fb::CFG_P32_X2 : rows <= 64 ? fb::CFG_P64_X2 : fb::CFG_P128_X2;
+  // up to 64 rows four 16-row waves, also for 32 rows, where the upper two
+  // only issue tile loads: every wave then issues half the loads, and the
+  // pass runs 5-8% faster than with two waves; 256-row KV heads take two
+  // 128-row tiles that share K/V through L2
+  return rows <= 64 ? fb::CFG_P64_X2 : fb::CFG_P128_X2;
 #endif
 }
 int block_cfg(const fb_desc* d) {

@@ -50,19 +50,29 @@ def test_block_bytes_and_flops_by_hand():
     assert bb == 1560 * 128 * 2 * (12 + 24) + 12 * 1560 * 129 * 4 + 1560 * 12 * 128 * 2
 
 
-def test_traffic_table_needs_the_same_kernel_source(tmp_path):
+def test_traffic_table_needs_the_same_library_sources(tmp_path):
     shutil.copy(os.path.join(ROOT, "bench.py"), tmp_path / "bench.py")
     (tmp_path / "profiles").mkdir()
     src = tmp_path / "cached_attention_amd" / "csrc"
     src.mkdir(parents=True)
-    (src / "fb_kernels.hip").write_text("// kernels v1\n")
-    sha = hashlib.sha256(b"// kernels v1\n").hexdigest()[:16]
+    files = {"fb_kernels.hip": "// kernels v1\n", "fb_api.cpp": "// planner v1\n", "fb_internal.h": "// h v1\n"}
+    for name, text in files.items():
+        (src / name).write_text(text)
+    h = hashlib.sha256()
+    for name in ("fb_kernels.hip", "fb_api.cpp", "fb_internal.h"):   # the hash, restated by hand
+        h.update(name.encode() + b"\0" + files[name].encode() + b"\0")
+    sha = h.hexdigest()[:16]
     (tmp_path / "profiles" / "hbm_traffic.md").write_text(
         "| workload | source | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes |\n|---|---|---|---|---|---|\n"
         f"| text_gqa_128k | {sha} | `k` | 1 | 2 | 720000000 |\n")
     b2 = _load_bench(str(tmp_path / "bench.py"))
+    assert b2.library_source_sha() == sha
     assert b2.measured_traffic("text_gqa_128k") == 720000000.0
     assert b2.measured_traffic("text_mha_32k") is None           # no row for it
+    (src / "fb_api.cpp").write_text("// planner v2\n")           # a configuration choice changed since
+    assert b2.measured_traffic("text_gqa_128k") is None
+    (src / "fb_api.cpp").write_text(files["fb_api.cpp"])
+    assert b2.measured_traffic("text_gqa_128k") == 720000000.0
     (src / "fb_kernels.hip").write_text("// kernels v2\n")        # the kernels changed since
     assert b2.measured_traffic("text_gqa_128k") is None
 
