@@ -62,10 +62,16 @@ int prefix_cfg(const fb_desc* d) {
 }
 int block_cfg(const fb_desc* d) {
   const int rows = (d->hq / d->hkv) * d->block_len;
-#ifdef FB_BLOCK_CFG_BIG
-  return rows >= 1024 ? FB_BLOCK_CFG_BIG : fb::CFG_B64;
+#if defined(FB_BLOCK_CFG_BIG) && defined(FB_BLOCK_CFG_SMALL)
+  // build-time override (used to sweep configurations)
+  return rows >= 1024 ? FB_BLOCK_CFG_BIG : FB_BLOCK_CFG_SMALL;
 #else
-  return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B64;
+  // measured on MI355X: text blocks are latency-bound, and 32-row workgroups
+  // of two row waves plus two waves that only issue tile loads run them
+  // fastest (more workgroups than 64-row ones, and each wave issues half the
+  // loads of a 2-wave workgroup); the 1560-row video block is MFMA-bound and
+  // takes 8 waves of 16 rows
+  return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B32_LD;
 #endif
 }
 // fp32 inputs run the VALU kernel: 64 rows per workgroup, 2 per CU.

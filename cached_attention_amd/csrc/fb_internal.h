@@ -12,23 +12,26 @@ constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
 
 // bf16 kernel configurations.  X(id, rows per wave / 16, waves, LDS stages,
 // resident workgroups per CU, pass: 1 = split partial of the prefix pass,
-// 0 = block pass with merge).  Query rows per workgroup = waves * 16 *
-// (rows per wave / 16).
+// 0 = block pass with merge, row waves: the first this many waves hold query
+// rows, the others only issue their share of the tile loads).  Query rows
+// per workgroup = row waves * 16 * (rows per wave / 16).
 #define FB_BF16_CFGS(X)                                                \
-  X(0, 1, 2, 4, 1, 1)    /* prefix  32 rows: 2 waves x 16            */ \
-  X(1, 1, 4, 4, 1, 1)    /* prefix  64 rows: 4 waves x 16            */ \
-  X(2, 2, 4, 4, 1, 1)    /* prefix 128 rows: 4 waves x 32            */ \
-  X(3, 2, 8, 4, 1, 1)    /* prefix 256 rows: 8 waves x 32            */ \
-  X(4, 1, 4, 2, 2, 0)    /* block   64 rows                          */ \
-  X(5, 1, 8, 2, 1, 0)    /* block  128 rows                          */ \
-  X(7, 2, 4, 2, 2, 1)    /* prefix 128 rows, 2 workgroups per CU     */ \
-  X(8, 4, 4, 4, 1, 1)    /* prefix 256 rows: 4 waves x 64            */ \
-  X(9, 1, 2, 2, 2, 1)    /* prefix  32 rows, 2 workgroups per CU     */ \
-  X(10, 1, 4, 2, 2, 1)   /* prefix  64 rows, 2 workgroups per CU     */ \
-  X(12, 1, 8, 4, 1, 1)   /* prefix 128 rows: 8 waves x 16            */ \
-  X(18, 2, 8, 2, 1, 0)   /* block  256 rows: 8 waves x 32            */ \
-  X(19, 2, 4, 2, 2, 0)   /* block  128 rows, 2 workgroups per CU     */ \
-  X(20, 4, 4, 4, 1, 0)   /* block  256 rows: 4 waves x 64            */
+  X(0, 1, 2, 4, 1, 1, 2)      /* prefix  32 rows: 2 waves x 16            */ \
+  X(1, 1, 4, 4, 1, 1, 4)      /* prefix  64 rows: 4 waves x 16            */ \
+  X(2, 2, 4, 4, 1, 1, 4)      /* prefix 128 rows: 4 waves x 32            */ \
+  X(3, 2, 8, 4, 1, 1, 8)      /* prefix 256 rows: 8 waves x 32            */ \
+  X(4, 1, 4, 2, 2, 0, 4)      /* block   64 rows                          */ \
+  X(5, 1, 8, 2, 1, 0, 8)      /* block  128 rows                          */ \
+  X(7, 2, 4, 2, 2, 1, 4)      /* prefix 128 rows, 2 workgroups per CU     */ \
+  X(8, 4, 4, 4, 1, 1, 4)      /* prefix 256 rows: 4 waves x 64            */ \
+  X(9, 1, 2, 2, 2, 1, 2)      /* prefix  32 rows, 2 workgroups per CU     */ \
+  X(10, 1, 4, 2, 2, 1, 4)     /* prefix  64 rows, 2 workgroups per CU     */ \
+  X(12, 1, 8, 4, 1, 1, 8)     /* prefix 128 rows: 8 waves x 16            */ \
+  X(18, 2, 8, 2, 1, 0, 8)     /* block  256 rows: 8 waves x 32            */ \
+  X(19, 2, 4, 2, 2, 0, 4)     /* block  128 rows, 2 workgroups per CU     */ \
+  X(20, 4, 4, 4, 1, 0, 4)     /* block  256 rows: 4 waves x 64            */ \
+  X(21, 1, 2, 2, 2, 0, 2)     /* block   32 rows: 2 waves x 16            */ \
+  X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */
 
 enum KernelCfg : int32_t {
   CFG_P32 = 0,
@@ -45,6 +48,8 @@ enum KernelCfg : int32_t {
   CFG_B256 = 18,
   CFG_B128_X2 = 19,
   CFG_B256_Q4 = 20,
+  CFG_B32 = 21,
+  CFG_B32_LD = 22,
 };
 
 struct CfgInfo {
@@ -53,8 +58,8 @@ struct CfgInfo {
 };
 inline CfgInfo cfg_info(int cfg) {
   switch (cfg) {
-#define FB_CFG_INFO(ID, QT, NW, NS, WPC, PART) \
-    case ID: return {(NW) * 16 * (QT), WPC};
+#define FB_CFG_INFO(ID, QT, NW, NS, WPC, PART, RW) \
+    case ID: return {(RW) * 16 * (QT), WPC};
     FB_BF16_CFGS(FB_CFG_INFO)
 #undef FB_CFG_INFO
     default: return {64, 1};

@@ -317,12 +317,13 @@ __device__ __forceinline__ void mfma_prio() {
   if constexpr (FB_MFMA_PRIO != 0) __builtin_amdgcn_s_setprio(P);
 }
 
-template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL>
+template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL, int RW>
 __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the score MFMA
   constexpr int DT = D / 16;                  // 16-row d tiles of O^T
   constexpr int CH = D / 8;                   // 16-byte slots per key row
-  constexpr int ROWS = NW * 16 * QT;          // query rows per workgroup
+  constexpr int ROWS = RW * 16 * QT;          // query rows per workgroup (waves 0 .. RW-1)
+  static_assert(RW >= 1 && RW <= NW, "row waves");
   constexpr int TBYTES = kTile * D * 2;       // one K or V tile
   constexpr int STAGE = 2 * TBYTES;
   constexpr int IPT = TBYTES / 1024;          // 1 KB direct-to-LDS loads per tile and tensor
@@ -348,12 +349,13 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 
   // ---- query fragments (B operand of the score MFMA) ----
   const int row_w0 = wk.rt * ROWS + wave * 16 * QT;
-  const bool wave_active = row_w0 < a.rows;
+  const bool row_wave = wave < RW;            // waves RW .. NW-1 only load tiles
+  const bool wave_active = row_wave && row_w0 < a.rows;
   bf16x8 qf[QT][KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int row = row_w0 + qt * 16 + l16;
-    if (row < a.rows) {
+    if (row_wave && row < a.rows) {
       const int h = wk.g * a.G + row / a.Lb;
       const int pos = row % a.Lb;
       const __bf16* qp = (const __bf16*)a.q + (int64_t)wk.b * a.q_sb + (int64_t)pos * a.q_st +
@@ -384,7 +386,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       le_pre[qt] = kNegInf;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) ext_pre[qt][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (row < a.rows) {
+      if (row_wave && row < a.rows) {
         const int64_t crow = ((int64_t)wk.b * a.Hq + wk.g * a.G + row / a.Lb) * a.Lb + row % a.Lb;
         if (a.ext_lse) le_pre[qt] = a.ext_lse[crow];
         if (a.ext_o) {
@@ -1495,10 +1497,10 @@ __global__ void __launch_bounds__(256) nan_scan_kernel(const float* x, int64_t n
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int D, int QT, int NW, int NS, int WPC, bool P>
+template <int D, int QT, int NW, int NS, int WPC, bool P, int RW>
 static int launch_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int minw = (NW * WPC + 3) / 4;   // waves per SIMD when WPC workgroups share a CU
-  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, minw, P>), dim3(a.grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, minw, P, RW>), dim3(a.grid), dim3(64 * NW), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -1511,8 +1513,8 @@ static int launch_f32(const AttnArgs& a, hipStream_t s) {
 template <int D>
 static int launch_bf16_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
   switch (cfg) {
-#define FB_CFG_LAUNCH(ID, QT, NW, NS, WPC, PART) \
-    case ID: return launch_bf16<D, QT, NW, NS, WPC, (PART) != 0>(a, s);
+#define FB_CFG_LAUNCH(ID, QT, NW, NS, WPC, PART, RW) \
+    case ID: return launch_bf16<D, QT, NW, NS, WPC, (PART) != 0, RW>(a, s);
     FB_BF16_CFGS(FB_CFG_LAUNCH)
 #undef FB_CFG_LAUNCH
     default: return (int)hipErrorInvalidValue;
