@@ -199,8 +199,10 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 // bf16 attention on MFMA
 // ---------------------------------------------------------------------------
 //
-// Workgroup: NW waves; wave w owns 16*QT consecutive query rows of one KV head
-// (row i -> query head g*G + i / Lb, block position i % Lb).  Per 64-key tile:
+// Workgroup: NW waves; wave w < RW owns 16*QT consecutive query rows of one KV
+// head (row i -> query head g*G + i / Lb, block position i % Lb); waves RW ..
+// NW-1 hold no rows and only issue their share of the tile loads.  Per
+// 64-key tile:
 //   S^T[key][q] = K Q^T      v_mfma_f32_16x16x32_bf16, A = K from LDS,
 //                            B = Q^T held in VGPRs for the whole pass
 //   online softmax on S^T    each lane holds one query column (lane & 15) and
