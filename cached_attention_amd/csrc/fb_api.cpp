@@ -74,7 +74,7 @@ int block_cfg(const fb_desc* d) {
   return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B32_LD;
 #endif
 }
-// fp32 inputs run the VALU kernel: 64 rows per workgroup, 2 per CU.
+// fp32 inputs run the fp32 MFMA kernel: 64 rows per workgroup (4 waves x 16), 2 per CU.
 fb::CfgInfo pass_info(const fb_desc* d, int cfg) {
   if (d->dtype == FB_F32) return {64, 2};
   return fb::cfg_info(cfg);
@@ -177,7 +177,7 @@ fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len
     for (int b = 0; b < d->batch; ++b) n += ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles), st_);
     return n * units;
   };
-  // (the fp32 kernel runs one wave per workgroup and gains from splits of one tile)
+  // (fp32 keeps splits of one tile: more workgroups for its small shapes)
   const int64_t min_split = d->dtype == FB_F32 ? 1 : kMinSplitTiles;
   int64_t st = std::max<int64_t>(min_split, ceil_div(total_tiles * units, capacity));
   while (st < max_tiles && wgs_for(st) > capacity) ++st;

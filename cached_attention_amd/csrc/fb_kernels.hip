@@ -9,7 +9,7 @@
 //                  one split per stream over its Lb block keys, merged in
 //                  registers with the cached (A_out, L_out) by the page's merge
 //                  equation and written in bf16.
-// attn_f32   -- the same two passes in plain fp32 VALU arithmetic.
+// attn_f32m  -- the same two passes in fp32 on v_mfma_f32_16x16x4_f32.
 // combine    -- log-sum-exp combination of the split partials (the merge
 //              equation generalised to n partials), optionally folding in one
 //              more partial (the sparse variant's cached residual).
@@ -751,97 +751,144 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 attention (plain VALU): one wave per workgroup, one query row per lane
+// fp32 attention on MFMA (v_mfma_f32_16x16x4_f32)
 // ---------------------------------------------------------------------------
-
+//
+// Workgroup: 4 waves x 16 query rows of one KV head (the 64-row tiles of the
+// host plan).  Per 64-key tile, staged in LDS with rows padded by 4 floats:
+//   S^T[key][q] = K Q^T    A = K from LDS, B = Q^T held in registers; in
+//                          k-step ks lane group lg takes dim lg*(D/4) + ks,
+//                          so each lane's K and Q values are contiguous
+//   online softmax         each lane holds one query column (l16) and keys
+//                          16*tt + 4*lg + r; running row max, O rescaled
+//   O^T[d][q] += V^T P^T   k-step (tt, r) takes key 16*tt + 4*lg + r in lane
+//                          group lg -- the lane's own p, no cross-lane move;
+//                          row m of d-tile dt is dim m*DT + dt, so each
+//                          lane's V reads are contiguous
+// Products and sums stay in fp32 throughout.
 template <int D, bool PARTIAL>
-__global__ void __launch_bounds__(64) attn_f32(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float Kt[kTile][D];
-  __shared__ __attribute__((aligned(16))) float Vt[kTile][D];
+__global__ void __launch_bounds__(256) attn_f32m(const AttnArgs a) {
+  constexpr int QQ = D / 4;     // dims per lane group = k-steps of the score MFMA
+  constexpr int DT = D / 16;    // d tiles of O^T
+  constexpr int LDK = D + 4;    // padded LDS row, floats
+  __shared__ __attribute__((aligned(16))) float Ks[kTile * LDK];
+  __shared__ __attribute__((aligned(16))) float Vs[kTile * LDK];
   Work wk;
   if (!decode_work<4>(a, wk)) return;
   if (a.head_mask && ld_const(a.head_mask, (int64_t)wk.b * a.Hkv + wk.g) == 0) return;   // cache reused
-  const int lane = threadIdx.x;
-  const int row = wk.rt * 64 + lane;
-  const bool active = row < a.rows;
-  int h = 0, pos = 0;
-  float q[D], acc[D];
-  if (active) {
-    h = wk.g * a.G + row / a.Lb;
-    pos = row % a.Lb;
-    const float* qp = (const float*)a.q + (int64_t)wk.b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int row = wk.rt * 64 + wave * 16 + l16;   // this lane's query column
+  const bool rvalid = row < a.rows;
+  const bool wave_active = wk.rt * 64 + wave * 16 < a.rows;
+  const int h = rvalid ? wk.g * a.G + row / a.Lb : 0;
+  const int pos = rvalid ? row % a.Lb : 0;
+  float qv[QQ];
 #pragma unroll
-    for (int d = 0; d < D; d += 4) {
-      const f32x4 v = *(const f32x4*)(qp + d);
-      q[d] = v[0]; q[d + 1] = v[1]; q[d + 2] = v[2]; q[d + 3] = v[3];
+  for (int i = 0; i < QQ; ++i) qv[i] = 0.f;
+  if (rvalid) {
+    const float* qp = (const float*)a.q + (int64_t)wk.b * a.q_sb + (int64_t)pos * a.q_st + (int64_t)h * a.q_sh +
+                      lg * QQ;
+#pragma unroll
+    for (int i = 0; i < QQ; i += 4) {
+      const f32x4 v = *(const f32x4*)(qp + i);
+      qv[i] = v[0]; qv[i + 1] = v[1]; qv[i + 2] = v[2]; qv[i + 3] = v[3];
     }
   }
+  f32x4 oacc[DT];
 #pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;   // l_run: this lane's keys only, summed over lane groups at the end
   const float c = a.c_log2;
   const int64_t row_bytes = a.kv_st * 4;
   int64_t tok0;
   int nvalid;
   while (next_tile(wk.it, tok0, nvalid)) {
-    __syncthreads();
-    for (int idx = lane; idx < kTile * (D / 4); idx += 64) {
+    __syncthreads();   // every wave is done with the previous tile
+    for (int idx = tid; idx < kTile * (D / 4); idx += 256) {
       const int t = idx / (D / 4), ch = idx % (D / 4);
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};   // keys past the end: zeros
       if (t < nvalid) {
         kv = *(const f32x4*)(wk.kbase + (tok0 + t) * row_bytes + ch * 16);
         vv = *(const f32x4*)(wk.vbase + (tok0 + t) * row_bytes + ch * 16);
       }
-      *(f32x4*)&Kt[t][ch * 4] = kv;
-      *(f32x4*)&Vt[t][ch * 4] = vv;
+      *(f32x4*)&Ks[t * LDK + ch * 4] = kv;
+      *(f32x4*)&Vs[t * LDK + ch * 4] = vv;
     }
     __syncthreads();
-    if (!active) continue;
-    // KG keys at a time: KG independent dot-product chains, one rescale per group
-    constexpr int KG = 8;
-    for (int t = 0; t < nvalid; t += KG) {
-      float sc[KG];
+    if (!wave_active) continue;
+    f32x4 s[4];
 #pragma unroll
-      for (int j = 0; j < KG; ++j) sc[j] = 0.f;
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      const float* kp = &Ks[(16 * tt + l16) * LDK + lg * QQ];
 #pragma unroll
-      for (int d = 0; d < D; ++d)
+      for (int i = 0; i < QQ; i += 4) {
+        const f32x4 kk = *(const f32x4*)(kp + i);
 #pragma unroll
-        for (int j = 0; j < KG; ++j) sc[j] = __builtin_fmaf(q[d], Kt[t + j][d], sc[j]);
-      float mx = kNegInf;
-#pragma unroll
-      for (int j = 0; j < KG; ++j) {
-        sc[j] = t + j < nvalid ? sc[j] * c : kNegInf;
-        mx = fmaxf(mx, sc[j]);
-      }
-      const float m_new = fmaxf(m_run, mx);   // finite: key t is valid
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
-      float p[KG], ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < KG; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sc[j] - m_new);
-        ps += p[j];
-      }
-      m_run = m_new;
-      l_run = l_run * alpha + ps;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        float a_d = acc[d] * alpha;
-#pragma unroll
-        for (int j = 0; j < KG; ++j) a_d = __builtin_fmaf(p[j], Vt[t + j][d], a_d);
-        acc[d] = a_d;
+        for (int u = 0; u < 4; ++u) s[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[u], qv[i + u], s[tt], 0, 0, 0);
       }
     }
+    // online softmax in the log2 domain
+    float mx = kNegInf;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 16 * tt + 4 * lg + r;
+        s[tt][r] = key < nvalid ? s[tt][r] * c : kNegInf;
+        mx = fmaxf(mx, s[tt][r]);
+      }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m_run, mx);   // finite: the tile has a valid key
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[tt][r] = __builtin_amdgcn_exp2f(s[tt][r] - m_new);
+        ps += s[tt][r];
+      }
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* vp = &Vs[(16 * tt + 4 * lg + r) * LDK + l16 * DT];
+#pragma unroll
+        for (int d4 = 0; d4 < DT; d4 += 4) {
+          const f32x4 vv = *(const f32x4*)(vp + d4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            oacc[d4 + u] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[u], s[tt][r], oacc[d4 + u], 0, 0, 0);
+        }
+      }
   }
-  if (!active) return;
-  const bool any = l_run > 0.f;
-  const float inv = any ? 1.f / l_run : 0.f;
-  const float lse = any ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  if (!wave_active) return;
+  float l = l_run;
+  l += shfl_xor_f(l, 16);
+  l += shfl_xor_f(l, 32);
+  if (!rvalid) return;
+  const bool any = l > 0.f;
+  const float inv = any ? 1.f / l : 0.f;
+  const float lse = any ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+  // lane (l16, lg) holds O^T rows 4*lg + i of every d tile: dims (4*lg + i)*DT + dt
   if constexpr (PARTIAL) {
     const int64_t prow = ((int64_t)wk.x * a.Hq + h) * a.Lb + pos;
     float* po = a.part_o + prow * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) po[d] = acc[d] * inv;
-    a.part_lse[prow] = lse;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) po[(4 * lg + i) * DT + dt] = oacc[dt][i] * inv;
+    if (lg == 0) a.part_lse[prow] = lse;
   } else {
     const int64_t crow = ((int64_t)wk.b * a.Hq + h) * a.Lb + pos;
     const float le = a.ext_lse ? a.ext_lse[crow] : kNegInf;
@@ -852,12 +899,15 @@ __global__ void __launch_bounds__(64) attn_f32(const AttnArgs a) {
     float* op = (float*)a.o + (((int64_t)wk.b * a.Lb + pos) * a.Hq + h) * D;
     const float* ep = a.ext_o ? a.ext_o + crow * D : nullptr;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      float r = wi * acc[d] * inv;
-      if (ep) r += we * ep[d];
-      op[d] = r / den;
-    }
-    if (a.lse_out) a.lse_out[crow] = mm + logf(den);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = (4 * lg + i) * DT + dt;
+        float r = wi * oacc[dt][i] * inv;
+        if (ep) r += we * ep[d];
+        op[d] = r / den;
+      }
+    if (lg == 0 && a.lse_out) a.lse_out[crow] = mm + logf(den);
   }
 }
 
@@ -1508,7 +1558,7 @@ static int launch_bf16(const AttnArgs& a, hipStream_t s) {
 
 template <int D, bool P>
 static int launch_f32(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_f32<D, P>), dim3(a.grid), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((attn_f32m<D, P>), dim3(a.grid), dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 

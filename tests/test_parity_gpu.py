@@ -27,10 +27,27 @@ def dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device="cuda", dtype=dtype)
 
 
-def tol(w, ref):
+def tol(w, ref, lse=None):
+    """Output bound: bf16 2e-2 absolute; fp32 1e-5 relative to max|O|.
+
+    For fp32 the relative bound widens where the log-normalisers are large.
+    The partials travel through the split combine and the cache merge as fp32
+    LSEs, and each rounding of an LSE of magnitude |L| is off by up to
+    |L|*2^-24 absolute.  That is a relative error of the same size in the
+    partial's merge weight.  Eight such roundings bound the chain (log2 to
+    natural log, the max shift, combine, merge), so the fp32 bound is
+    max(1e-5, 8 * 2^-24 * max|L|) relative.  For ordinary inputs, |L| <= 20,
+    this stays 1e-5.  It grows only for scores in the hundreds, as in the
+    score-jump case.
+    """
     if w.dtype == "bf16":
         return 2e-2
-    return 1e-5 * max(1.0, float(np.abs(ref).max()))
+    rel = 1e-5
+    if lse is not None:
+        finite = np.asarray(lse)[np.isfinite(lse)]
+        if finite.size:
+            rel = max(rel, 8 * 2.0 ** -24 * float(np.abs(finite).max()))
+    return rel * max(1.0, float(np.abs(ref).max()))
 
 
 def tol_lse(w, ref_lse):
@@ -73,7 +90,7 @@ def check_block(w, prefix, blk, r, mode, chunks=None, check_cache=True):
                            mode=mode, chunks=chunks)
     got = run_gpu(w, prefix, blk, r, mode, chunks)
     for s in range(w.steps):
-        tl = tol(w, ref.out[s])
+        tl = tol(w, ref.out[s], ref.lse[s])
         err = np.abs(got.out[s] - ref.out[s]).max()
         assert err <= tl, f"step {s}: max|O - O_ref| = {err:.3e} > {tl:.1e}"
         lerr = np.abs(got.lse[s] - ref.lse[s]).max()
