@@ -66,12 +66,14 @@ int block_cfg(const fb_desc* d) {
   // build-time override (used to sweep configurations)
   return rows >= 1024 ? FB_BLOCK_CFG_BIG : FB_BLOCK_CFG_SMALL;
 #else
-  // measured on MI355X: text blocks are latency-bound, and 32-row workgroups
-  // of two row waves plus two waves that only issue tile loads run them
-  // fastest (more workgroups than 64-row ones, and each wave issues half the
-  // loads of a 2-wave workgroup); the 1560-row video block is MFMA-bound and
-  // takes 8 waves of 16 rows
-  return rows >= 1024 ? fb::CFG_B128 : fb::CFG_B32_LD;
+  // measured on MI355X: the 1560-row video block is MFMA-bound and takes 8
+  // waves of 16 rows.  Text blocks are latency-bound and run fastest on
+  // 4-wave workgroups whose extra waves only issue tile loads: 16 rows (one
+  // row wave) while that gives at most one workgroup per CU, else 32 rows
+  // (two row waves), which beat 16-row ones once those fill the CUs twice.
+  if (rows >= 1024) return fb::CFG_B128;
+  const int64_t wgs16 = (int64_t)d->batch * d->hkv * ceil_div(rows, 16);
+  return wgs16 <= kCUs ? fb::CFG_B16_LD : fb::CFG_B32_LD;
 #endif
 }
 // fp32 inputs run the fp32 MFMA kernel: 64 rows per workgroup (4 waves x 16), 2 per CU.

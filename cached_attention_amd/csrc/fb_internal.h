@@ -31,7 +31,8 @@ constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
   X(19, 2, 4, 2, 2, 0, 4)     /* block  128 rows, 2 workgroups per CU     */ \
   X(20, 4, 4, 4, 1, 0, 4)     /* block  256 rows: 4 waves x 64            */ \
   X(21, 1, 2, 2, 2, 0, 2)     /* block   32 rows: 2 waves x 16            */ \
-  X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */
+  X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */ \
+  X(26, 1, 4, 2, 2, 0, 1)     /* block   16 rows + 3 loading waves        */
 
 enum KernelCfg : int32_t {
   CFG_P32 = 0,
@@ -50,6 +51,7 @@ enum KernelCfg : int32_t {
   CFG_B256_Q4 = 20,
   CFG_B32 = 21,
   CFG_B32_LD = 22,
+  CFG_B16_LD = 26,
 };
 
 struct CfgInfo {
