@@ -60,7 +60,7 @@ def scale_of(w):
     return 1.0 / math.sqrt(w.head_dim)
 
 
-class GpuRun:
+class GpuResult:
     def __init__(self):
         self.out, self.lse, self.o_ext, self.lse_ext, self.refreshed = [], [], [], [], []
 
@@ -72,7 +72,7 @@ def run_gpu(w, prefix, blk, r=1, mode="cached", chunks=None, st=None, k_pre=None
                            chunks=None if chunks is None else torch.from_numpy(chunks))
     kp = dev(prefix.k, t) if k_pre is None else k_pre
     vp = dev(prefix.v, t) if v_pre is None else v_pre
-    res = GpuRun()
+    res = GpuResult()
     for s in range(blk.q.shape[0]):
         q, k, v = dev(blk.q[s], t), dev(blk.k[s], t), dev(blk.v[s], t)
         res.refreshed.append(st.step(q, k, v, kp, vp, s, r, mode))
