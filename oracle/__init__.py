@@ -21,7 +21,10 @@ permutations), the partition invariant of the merge, cached mode at r = 1
 against full recompute, and the refresh schedule.  The adaptive reuse policies
 (``policies.py``) are pinned by constructed update counts and similarities,
 their extreme thresholds against full recompute and against never refreshing,
-and a per-head partition of given masks.  The block append is pinned against
+and a per-head partition of given masks.  Sparse attention without the
+residual (``sparse_only_step``) is pinned by its two extremes, every chunk
+selected (the library routine over the whole prefix) and none (over the block
+alone), and by brute force over the selected tokens.  The block append is pinned against
 direct concatenation, and chunk selection by constructed pooled means, the
 max over a KV group's queries, ties to the lower index and a brute-force
 check of the kept set.  Cached mode at r > 1 is an

@@ -264,8 +264,12 @@ def run_block(k_pre, v_pre, offsets, q_steps, k_steps, v_steps, scale: float,
 
 
 def sparse_only_step(q_blk, k_blk, v_blk, k_pre, v_pre, offsets, scale, chunks, chunk_len=64):
-    """Context baseline: sparse attention without the cached residual
-    (selected chunks + block only).  Returns O [B][Lb][Hq][D]."""
+    """Context baseline: sparse attention without the cached residual.
+
+    The keys are the selected chunks of the prefix (per stream and KV head,
+    clipped to the prefix) and the block's own keys; the unselected chunks,
+    whose contribution the sparse variant keeps as its residual, are left out
+    entirely.  Returns O [B][Lb][Hq][D]."""
     sel_o, sel_l = prefix_partial(q_blk, k_pre, v_pre, offsets, scale, chunks, chunk_len, "selected")
     in_o, in_l = block_partial(q_blk, k_blk, v_blk, scale)
     o, _ = merge(sel_o, sel_l, in_o, in_l)

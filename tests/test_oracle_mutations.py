@@ -38,6 +38,13 @@ MUTATIONS = {
                                "return np.nonzero(~sel)[0][:-1]"),
     "chunk_end_off_by_one": ("attention.py", "sel[c * chunk_len: min((c + 1) * chunk_len, lp)] = True",
                              "sel[c * chunk_len: min((c + 1) * chunk_len - 1, lp)] = True"),
+    # sparse attention without the cached residual (the merge itself is
+    # symmetric in its two partials, so an operand swap there is no mistake)
+    "sparse_only_complement": ("attention.py",
+                               'prefix_partial(q_blk, k_pre, v_pre, offsets, scale, chunks, chunk_len, "selected")',
+                               'prefix_partial(q_blk, k_pre, v_pre, offsets, scale, chunks, chunk_len, "complement")'),
+    "sparse_only_drops_block": ("attention.py", "o, _ = merge(sel_o, sel_l, in_o, in_l)", "o = sel_o"),
+    "sparse_only_drops_selected": ("attention.py", "o, _ = merge(sel_o, sel_l, in_o, in_l)", "o = in_o"),
     # growing the prefix with a finalised block
     "grow_v_from_k": ("attention.py", "vs.append(v_last[b])", "vs.append(k_last[b])"),
     "append_v_from_k": ("attention.py", "v_new[r0:r0 + lb] = v_last[b]", "v_new[r0:r0 + lb] = k_last[b]"),

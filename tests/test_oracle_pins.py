@@ -402,6 +402,58 @@ def test_sparse_cached_r1_equals_full():
     assert np.abs(so - full.out[0]).max() > 1e-3
 
 
+# sparse attention without the cached residual: the selected chunks plus the
+# block, nothing else (the context baseline of the sparse-compatibility reading)
+
+@pytest.mark.parametrize("chunk_len", [64, 16])
+def test_sparse_only_every_chunk_is_full_attention(chunk_len):
+    """Selecting every chunk leaves nothing out: the library routine over the
+    whole prefix plus the block (ragged streams, GQA, a partial last chunk)."""
+    w, p, blk = _tiny_block(seed=21, steps=1, lp=150, ragged=True)
+    q, kb, vb, kp, vp = (np.float64(x) for x in (blk.q[0], blk.k[0], blk.v[0], p.k, p.v))
+    scale = 1 / math.sqrt(w.head_dim)
+    n_max = max(-(-int(p.offsets[b + 1] - p.offsets[b]) // chunk_len) for b in range(w.batch))
+    # indices past a shorter stream's end select nothing there
+    chunks = np.broadcast_to(np.arange(n_max, dtype=np.int32), (w.batch, w.hkv, n_max))
+    so = oracle.sparse_only_step(q, kb, vb, kp, vp, p.offsets, scale, chunks, chunk_len)
+    o_ref, _ = _sdpa_full(q, kb, vb, kp, vp, p.offsets, scale)
+    np.testing.assert_allclose(so, o_ref, rtol=0, atol=1e-12)
+
+
+def test_sparse_only_no_chunk_is_block_attention():
+    """An empty selection keeps only the block's own keys: the library routine
+    over the block alone (an empty prefix)."""
+    w, p, blk = _tiny_block(seed=22, steps=1, lp=150, ragged=True)
+    q, kb, vb, kp, vp = (np.float64(x) for x in (blk.q[0], blk.k[0], blk.v[0], p.k, p.v))
+    scale = 1 / math.sqrt(w.head_dim)
+    chunks = np.zeros((w.batch, w.hkv, 0), dtype=np.int32)
+    so = oracle.sparse_only_step(q, kb, vb, kp, vp, p.offsets, scale, chunks)
+    no_prefix = np.zeros(w.batch + 1, dtype=np.int64)
+    o_ref, _ = _sdpa_full(q, kb, vb, kp[:0], vp[:0], no_prefix, scale)
+    np.testing.assert_allclose(so, o_ref, rtol=0, atol=1e-12)
+
+
+def test_sparse_only_brute_force_tiny():
+    """Pure-Python loops over exactly the selected chunks' tokens and the block's
+    tokens, per KV head with its own chunk list (4-token chunks, a ragged last one)."""
+    rng = np.random.default_rng(23)
+    d, lp, lb, hq, hkv, cl = 8, 15, 3, 4, 2, 4
+    k_pre, v_pre = _rand(rng, lp, hkv, d), _rand(rng, lp, hkv, d)
+    offsets = np.array([0, lp], dtype=np.int64)
+    q = _rand(rng, 1, lb, hq, d)
+    kb, vb = _rand(rng, 1, lb, hkv, d), _rand(rng, 1, lb, hkv, d)
+    chunks = np.array([[[0, 3], [1, 2]]], dtype=np.int32)   # KV head 1 keeps tokens 4..11
+    scale = 0.4
+    so = oracle.sparse_only_step(q, kb, vb, k_pre, v_pre, offsets, scale, chunks, cl)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        toks = [t for c in chunks[0][g].tolist() for t in range(c * cl, min((c + 1) * cl, lp))]
+        keys = np.concatenate([k_pre[toks, g], kb[0, :, g]])
+        vals = np.concatenate([v_pre[toks, g], vb[0, :, g]])
+        bo, _ = _brute(q[0, :, h], keys, vals, scale)
+        np.testing.assert_allclose(so[0, :, h], bo, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # growing prefix
 # ---------------------------------------------------------------------------
