@@ -17,6 +17,12 @@ whole KV cache), the cached-vs-full speedup, per-step latencies, the
 cached-vs-recompute drift, the prefix kernel against the HBM roofline, and the
 fp64 oracle timed on the host cores as a baseline.
 
+The default workload is the long-context GQA text layer (32 query / 8 KV
+heads, head_dim 128, 64-token block, 128K-token prefix, 8 steps, r = 8).  The
+roofline object covers the prefix pass: the split-KV kernel (K1) and the split
+combine (K2) together, timed back to back on the launch stream; K1 alone is
+reported beside it.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--r R]
 """
 from __future__ import annotations
@@ -61,22 +67,26 @@ def library_source_sha(root=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the prefix kernel from profiles/hbm_traffic.md, or None.
+def measured_traffic(workload, pass_name="prefix"):
+    """HBM bytes per launch of one pass from profiles/hbm_traffic.md, or None.
 
-    The table records the hash of the library sources the counters were taken
-    with (library_source_sha); a row only counts while they still hash the same.
+    The table has one row per kernel of a pass (the prefix pass: the split-KV
+    kernel and the split combine), with the hash of the library sources the
+    counters were taken with (library_source_sha); rows only count while the
+    sources still hash the same.  Returns the sum over the pass's rows.
     """
     here = os.path.dirname(os.path.abspath(__file__))
     table = os.path.join(here, "profiles", "hbm_traffic.md")
     sha = library_source_sha(here)
     if not os.path.exists(table) or sha is None:
         return None
+    total, rows = 0.0, 0
     for line in open(table):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 6 and cells[0] == workload and cells[1] == sha:
-            return float(cells[5])
-    return None
+        if len(cells) == 7 and cells[0] == workload and cells[1] == pass_name and cells[2] == sha:
+            total += float(cells[6])
+            rows += 1
+    return total if rows else None
 
 
 def smi_snapshot():
@@ -141,11 +151,13 @@ def blas_threads() -> int:
     return 1
 
 
-def cpu_baseline(w, prefix, blocks, r, budget_s=15.0, variant="fixed", k_sel=0, tau=0, eps=0.0, gamma=0.0):
+def cpu_baseline(w, prefix, blocks, r, budget_s=12.0, variant="fixed", k_sel=0, tau=0, eps=0.0, gamma=0.0):
     """The fp64 oracle (as it stands) on the same workload's first block, in
     the variant the GPU runs (fixed-period cached, sparse with the oracle's own
     chunk selection at the block's first step, or an adaptive reuse policy), on
-    the host cores; repeated until ~budget_s of CPU work."""
+    the host cores; repeated until ~budget_s of CPU work.  Full recompute is
+    sampled as the block's first step alone (every full step costs the same),
+    scaled to the block's steps."""
     import oracle
     scale = 1.0 / math.sqrt(w.head_dim)
     blk = blocks[0]
@@ -169,14 +181,31 @@ def cpu_baseline(w, prefix, blocks, r, budget_s=15.0, variant="fixed", k_sel=0, 
         if el >= budget_s or runs >= 100:
             break
     per_block = el / runs
+    t1 = time.perf_counter()
+    oracle.full_step(blk.q[0], blk.k[0], blk.v[0], prefix.k, prefix.v, prefix.offsets, scale)
+    full_step_s = time.perf_counter() - t1
     tok = w.batch * w.block_len * w.steps
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     return {
         "value": tok / per_block,
         "unit": "query-tok/s",
         "cores": blas_threads(),
+        "cpu_count": os.cpu_count(),
+        "sched_affinity": affinity,
+        "threads": {"blas": blas_threads(), "elementwise": 1,
+                    "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+                    "OPENBLAS_NUM_THREADS": os.environ.get("OPENBLAS_NUM_THREADS")},
         "kind": "oracle",
         "sample": f"{runs} x first block of {w.name} ({w.steps} steps, {variant}, r={r}, all streams and heads), "
-                  f"numpy fp64, {el:.1f} s; BLAS threads as cores, elementwise single-threaded",
+                  f"numpy fp64, {el:.1f} s; full recompute: the block's first step ({full_step_s:.1f} s) "
+                  f"x {w.steps} steps; cores = BLAS threads, elementwise work single-threaded",
+        "ms_per_block": per_block * 1e3,
+        "full_recompute": {"value": tok / (full_step_s * w.steps), "unit": "query-tok/s",
+                           "ms_per_block": full_step_s * w.steps * 1e3},
+        "speedup_vs_full": full_step_s * w.steps / per_block,
     }
 
 
@@ -185,7 +214,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30, help="timed bench steps (blocks)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="text_mha_32k")
+    ap.add_argument("--workload", default="text_gqa_128k")
     ap.add_argument("--r", type=int, default=8)
     ap.add_argument("--kv-layout", choices=("head", "token", "interleave"), default="head",
                     help="prefix KV cache layout: head-major [Hkv][T][D], token-major [T][Hkv][D], or head-major "
@@ -370,6 +399,26 @@ def main() -> int:
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n   # ms
 
+    def timed_graph(fn, n, reps=10):
+        """Device time per call of fn (ms): n back-to-back calls captured in one
+        graph, replayed reps times, so host launch overhead stays out of short
+        kernels.  The library only launches kernels (no memset, no allocation)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = timed(g.replay, reps) / n
+        del g
+        return ms
+
     gpu_idle = None if args.no_gpu_state else smi_snapshot()
     # ---- whole bench steps: cached (r) and full recompute ----
     for _ in range(args.warmup):
@@ -412,7 +461,8 @@ def main() -> int:
     med = lambda xs: float(np.median(xs)) if xs else None
     pct = lambda xs, q: float(np.percentile(xs, q)) if xs else None
 
-    # ---- the dominant kernel alone: split-KV prefix pass (fb_prefix_partials) ----
+    # ---- the dominant pass alone: split-KV prefix kernel (fb_prefix_partials,
+    # K1) + split combine into the fp32 cache (fb_prefix_combine, K2) ----
     q0 = steps_dev[0][0][0]
     n_k = max(20, args.steps)
     rot = [0]
@@ -426,13 +476,20 @@ def main() -> int:
         rot[0] += 1
         fbl.fb_prefix_partials(st0.desc, q0, kp, vp, sel, st0.ws, st0.ws_bytes)
 
-    for _ in range(3):
+    def combine():
+        fbl.fb_prefix_combine(st0.desc, sel, None, None, st0.o_ext, st0.lse_ext, st0.ws, st0.ws_bytes)
+
+    def prefix_pass():
         prefix_kernel()
+        combine()
+
+    for _ in range(3):
+        prefix_pass()
     ms_prefix_kernel = timed(prefix_kernel, n_k)
-    ms_combine = timed(lambda: fbl.fb_prefix_combine(st0.desc, sel, None, None, st0.o_ext, st0.lse_ext,
-                                                     st0.ws, st0.ws_bytes), n_k)
+    ms_prefix_pass = timed(prefix_pass, n_k)
+    ms_combine = timed_graph(combine, n_k)
     qb, kb, vb = steps_dev[0][1]
-    ms_block = timed(lambda: fbl.fb_block_attn(st0.desc, qb, kb, vb, st0.o_ext, st0.lse_ext, st0.o), n_k)
+    ms_block = timed_graph(lambda: fbl.fb_block_attn(st0.desc, qb, kb, vb, st0.o_ext, st0.lse_ext, st0.o), n_k)
     ms_select = ms_select_full = None
     if topk:
         sel_rot = [0]
@@ -486,10 +543,13 @@ def main() -> int:
     if args.sparse:
         sparse_tokens = sum(min(64 * k_sel, l) for l in lens)   # selected keys per KV head, all streams
     pb, pf, bb, bf = algorithmic(w, lens, sparse_tokens)
-    prefix_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
-    prefix_tflops = pf / (ms_prefix_kernel * 1e-3) / 1e12
+    # the pass (K1 + K2) is what the roofline reports; K1 alone sits beside it
+    prefix_gbs = pb / (ms_prefix_pass * 1e-3) / 1e9
+    prefix_tflops = pf / (ms_prefix_pass * 1e-3) / 1e12
+    k1_gbs = pb / (ms_prefix_kernel * 1e-3) / 1e9
+    k1_tflops = pf / (ms_prefix_kernel * 1e-3) / 1e12
 
-    # the dominant kernel's roofline: HBM below the ridge point, MFMA above it
+    # the dominant pass's roofline: HBM below the ridge point, MFMA above it
     mfma_bound = pf / pb > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": prefix_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -497,16 +557,22 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": prefix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": prefix_gbs / HBM_PEAK_GBS}
-    traffic = measured_traffic(w.name) if not args.sparse and args.kv_layout == "head" else None
+    traffic_key = f"{w.name}~sparse" if args.sparse else w.name
+    traffic = measured_traffic(traffic_key) if args.kv_layout == "head" and args.chunk_select == "topk" else None
     roof.update({
         "traffic": traffic,
-        "traffic_source": ("profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated, "
-                           "same kernel source)") if traffic is not None else None,
-        "kernel": "attn_bf16 prefix split-KV (fb_prefix_partials" + (", selected chunks)" if args.sparse else ")"),
+        "traffic_source": ("profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE + WRITE_SIZE per dispatch, "
+                           "copy-calibrated, K1 + K2, same library source)") if traffic is not None else None,
+        "kernel": ("prefix pass: attn_bf16 split-KV partials (fb_prefix_partials" +
+                   (", selected chunks" if args.sparse else "") + ") + combine_kernel (fb_prefix_combine)"),
+        "us_per_launch": ms_prefix_pass * 1e3,
         "algorithmic_bytes_per_launch": pb,
         "algorithmic_flops_per_launch": pf,
         "hbm_gbs": prefix_gbs, "hbm_frac": prefix_gbs / HBM_PEAK_GBS,
         "mfma_tflops": prefix_tflops, "mfma_frac": prefix_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "k1_only": {"kernel": "attn_bf16 split-KV partials (fb_prefix_partials)", "us": ms_prefix_kernel * 1e3,
+                    "hbm_gbs": k1_gbs, "hbm_frac": k1_gbs / HBM_PEAK_GBS,
+                    "mfma_tflops": k1_tflops, "mfma_frac": k1_tflops / MFMA_BF16_PEAK_TFLOPS},
     })
 
     result = {
@@ -547,10 +613,12 @@ def main() -> int:
                             "reuse_p10": pct(lat["reuse"], 10), "reuse_p90": pct(lat["reuse"], 90),
                             "samples": {"refresh": len(lat["refresh"]), "reuse": len(lat["reuse"])},
                             "launch_floor": ms_floor * 1e3},
-        "block_pass": {"us": ms_block * 1e3, "algorithmic_bytes": bb, "algorithmic_flops": bf,
+        "block_pass": {"us": ms_block * 1e3, "timing": "graph of back-to-back launches, replayed",
+                       "algorithmic_bytes": bb, "algorithmic_flops": bf,
                        "gbs": bb / (ms_block * 1e-3) / 1e9, "tflops": bf / (ms_block * 1e-3) / 1e12,
                        "mfma_frac": bf / (ms_block * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "kernels_us": {"prefix_splitkv": ms_prefix_kernel * 1e3, "split_combine": ms_combine * 1e3,
+                       "prefix_pass_k1_k2": ms_prefix_pass * 1e3,
                        "block_attn_merge": ms_block * 1e3,
                        "select_chunks": ms_select * 1e3 if ms_select is not None else None,
                        "select_chunks_full_pool": ms_select_full * 1e3 if ms_select_full is not None else None},

@@ -254,8 +254,13 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int k) {
   }
 }
 
+// The barrier that precedes a stage's refill.  Each wave first drains its own
+// LDS reads (lgkmcnt(0)): the V^T fragments of the deferred PV groups are read
+// from the stage the next direct-to-LDS loads overwrite, and nothing else
+// orders those reads before another wave's refill.
 __device__ __forceinline__ void lds_dma_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -284,11 +289,12 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* s
   const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t bs = ((uint64_t)b_hi << 32) | (uint64_t)b_lo;
+  // M0 (the LDS destination) is an explicit operand, so the compiler knows
+  // the asm sets it and keeps no live value of its own there
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "s"(l), "v"(voff), "s"(bs)
+      : "v"(voff), "s"(bs), "{m0}"(l)
       : "memory");
 }
 

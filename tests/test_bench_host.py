@@ -63,11 +63,18 @@ def test_traffic_table_needs_the_same_library_sources(tmp_path):
         h.update(name.encode() + b"\0" + files[name].encode() + b"\0")
     sha = h.hexdigest()[:16]
     (tmp_path / "profiles" / "hbm_traffic.md").write_text(
-        "| workload | source | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes |\n|---|---|---|---|---|---|\n"
-        f"| text_gqa_128k | {sha} | `k` | 1 | 2 | 720000000 |\n")
+        "| workload | pass | source | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes |\n"
+        "|---|---|---|---|---|---|---|\n"
+        f"| text_gqa_128k | prefix | {sha} | `k1` | 1 | 2 | 700000000 |\n"
+        f"| text_gqa_128k | prefix | {sha} | `k2` | 1 | 2 | 20000000 |\n"
+        f"| text_gqa_128k | block | {sha} | `k3` | 1 | 2 | 5000000 |\n"
+        f"| text_gqa_128k~sparse | prefix | {sha} | `k1` | 1 | 2 | 90000000 |\n")
     b2 = _load_bench(str(tmp_path / "bench.py"))
     assert b2.library_source_sha() == sha
+    # the prefix pass: the sum of its kernels' rows (split-KV partials + combine)
     assert b2.measured_traffic("text_gqa_128k") == 720000000.0
+    assert b2.measured_traffic("text_gqa_128k", "block") == 5000000.0
+    assert b2.measured_traffic("text_gqa_128k~sparse") == 90000000.0
     assert b2.measured_traffic("text_mha_32k") is None           # no row for it
     (src / "fb_api.cpp").write_text("// planner v2\n")           # a configuration choice changed since
     assert b2.measured_traffic("text_gqa_128k") is None
@@ -93,3 +100,6 @@ def test_cpu_baseline_runs_the_gpu_variant():
                         ("gamma", {"gamma": 0.99})]:
         r = bench.cpu_baseline(w, prefix, blocks, 2, budget_s=0.05, variant=variant, **kw)
         assert r["value"] > 0 and r["kind"] == "oracle" and f", {variant}, " in r["sample"]
+        # host cores as the OS reports them, and full recompute timed beside the cached block
+        assert r["cpu_count"] == os.cpu_count() and r["sched_affinity"] == len(os.sched_getaffinity(0))
+        assert r["cores"] >= 1 and r["full_recompute"]["value"] > 0 and r["speedup_vs_full"] > 0
