@@ -14,6 +14,7 @@
 #include "flashblock.h"
 
 static_assert(fb::kDtypeBf16 == FB_BF16, "dtype tag of the kernels");
+static_assert(fb::kNoAllocScratchBytes == FB_NOALLOC_SCRATCH_BYTES, "no-allocation scratch size");
 
 namespace {
 
@@ -486,14 +487,12 @@ static fb_status cache_has_nan(const fb_desc* d, const float* oc, const float* l
   return FB_OK;
 }
 
-extern "C" {
-
-fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
-                  const void* v_pre, const fb_sparse* sp, float* o_ext_cache, float* lse_ext_cache,
-                  float* o_res_cache, float* lse_res_cache, void* o, float* lse_out, int32_t step,
-                  int32_t refresh_period, int32_t mode, int32_t force_refresh, int32_t* refreshed_out, void* ws,
-                  size_t ws_bytes, void* stream) {
-  clear_error();
+// Argument checks of fb_step and fb_step_noalloc (everything but the
+// workspace); *need receives the workspace the step uses.
+static fb_status step_checks(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                             const void* k_pre, const void* v_pre, const fb_sparse* sp, float* o_ext_cache,
+                             float* lse_ext_cache, float* o_res_cache, float* lse_res_cache, void* o, int32_t step,
+                             int32_t refresh_period, int32_t mode, size_t* need) {
   fb_status st = check_desc(d);
   if (st == FB_OK) st = check_offsets(d);
   if (st == FB_OK) st = check_sparse(sp, false);
@@ -510,10 +509,17 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
   if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_pre) || !aligned16(v_pre) ||
       !aligned16(o_ext_cache) || !aligned16(o) || (sp && !aligned16(o_res_cache)))
     return fail(FB_ERR_ALIGN, "all tensor base pointers must be 16-byte aligned");
-  const size_t need = workspace_for(d, sp);
-  st = check_ws(ws, ws_bytes, need);
-  if (st != FB_OK) return st;
+  *need = workspace_for(d, sp);
+  return FB_OK;
+}
 
+// The step itself, after step_checks and a workspace of at least *need bytes.
+static fb_status step_run(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                          const void* k_pre, const void* v_pre, const fb_sparse* sp, float* o_ext_cache,
+                          float* lse_ext_cache, float* o_res_cache, float* lse_res_cache, void* o, float* lse_out,
+                          int32_t step, int32_t refresh_period, int32_t mode, int32_t force_refresh,
+                          int32_t* refreshed_out, void* ws, size_t ws_bytes, void* stream) {
+  fb_status st = FB_OK;
   const bool refresh = mode == FB_MODE_FULL || force_refresh != 0 || step % refresh_period == 0;
   if (refreshed_out) *refreshed_out = refresh ? 1 : 0;
   if (!refresh && debug_checks() && !capturing(stream)) {
@@ -540,6 +546,44 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
     if (st != FB_OK) return st;
   }
   return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
+}
+
+extern "C" {
+
+fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk, const void* k_pre,
+                  const void* v_pre, const fb_sparse* sp, float* o_ext_cache, float* lse_ext_cache,
+                  float* o_res_cache, float* lse_res_cache, void* o, float* lse_out, int32_t step,
+                  int32_t refresh_period, int32_t mode, int32_t force_refresh, int32_t* refreshed_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+  clear_error();
+  size_t need = 0;
+  fb_status st = step_checks(d, q_blk, k_blk, v_blk, k_pre, v_pre, sp, o_ext_cache, lse_ext_cache, o_res_cache,
+                             lse_res_cache, o, step, refresh_period, mode, &need);
+  if (st == FB_OK) st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+  return step_run(d, q_blk, k_blk, v_blk, k_pre, v_pre, sp, o_ext_cache, lse_ext_cache, o_res_cache, lse_res_cache,
+                  o, lse_out, step, refresh_period, mode, force_refresh, refreshed_out, ws, ws_bytes, stream);
+}
+
+fb_status fb_step_noalloc(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                          const void* k_pre, const void* v_pre, const fb_sparse* sp, float* o_ext_cache,
+                          float* lse_ext_cache, float* o_res_cache, float* lse_res_cache, void* o, float* lse_out,
+                          int32_t step, int32_t refresh_period, int32_t mode, int32_t force_refresh,
+                          int32_t* refreshed_out, void* stream) {
+  clear_error();
+  size_t need = 0;
+  fb_status st = step_checks(d, q_blk, k_blk, v_blk, k_pre, v_pre, sp, o_ext_cache, lse_ext_cache, o_res_cache,
+                             lse_res_cache, o, step, refresh_period, mode, &need);
+  if (st != FB_OK) return st;
+  if (need > fb::kNoAllocScratchBytes)
+    return fail(FB_ERR_WORKSPACE, "fb_step_noalloc: this shape needs %zu bytes of scratch, more than the %zu "
+                "bytes the library holds per GPU (use fb_step with a workspace)", need, fb::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = hip_status(fb::noalloc_scratch(&ws), "fb_step_noalloc scratch address");
+  if (st != FB_OK) return st;
+  return step_run(d, q_blk, k_blk, v_blk, k_pre, v_pre, sp, o_ext_cache, lse_ext_cache, o_res_cache, lse_res_cache,
+                  o, lse_out, step, refresh_period, mode, force_refresh, refreshed_out, ws, fb::kNoAllocScratchBytes,
+                  stream);
 }
 
 fb_status fb_refresh_mask_tau(const fb_desc* d, const void* k_prev, const void* v_prev, const void* k_cur,

@@ -1,6 +1,7 @@
 // Internal launch arguments shared by the host planner (fb_api.cpp) and the
 // kernels (fb_kernels.hip).  Not part of the public ABI.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fb {
@@ -179,5 +180,11 @@ int launch_select_pooled(const SelectArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
 // *flag = 1 if any of x[0..n) is NaN (flag cleared first when clear is set)
 int launch_nan_scan(const float* x, int64_t n, int32_t* flag, bool clear, void* stream);
+
+// Scratch of the no-allocation step: a file-scope device array of this many
+// bytes in fb_kernels.hip, one per GPU.  *ptr receives its address on the
+// calling thread's current device (looked up once per device, thread-safe).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+int noalloc_scratch(void** ptr);
 
 }  // namespace fb

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fb_internal.h"
 
 namespace fb {
@@ -1549,6 +1551,39 @@ __global__ void __launch_bounds__(256) nan_scan_kernel(const float* x, int64_t n
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     bad |= __builtin_isnan(x[i]);
   if (bad) *flag = 1;
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the no-allocation step (fb_step_noalloc)
+// ---------------------------------------------------------------------------
+//
+// The split partials of the prefix pass normally live in a caller workspace.
+// For callers that cannot allocate, they live here instead: every GPU the
+// library runs on holds this array from the module's load until the process
+// ends, and every call on that GPU shares it.  In host code the array's name
+// is only a host-side stand-in: its device address on each GPU comes from
+// hipGetSymbolAddress with that GPU current, and only that address is passed
+// to kernels.
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 // ---------------------------------------------------------------------------

@@ -24,7 +24,8 @@ FB_MODE_CACHED, FB_MODE_FULL = 0, 1
 FB_CHUNKS_SELECTED, FB_CHUNKS_COMPLEMENT = 1, 2
 
 EXPORTS = ("fb_workspace_size", "fb_prefix_attn", "fb_prefix_partials", "fb_prefix_combine",
-           "fb_block_attn", "fb_merge", "fb_step", "fb_refresh_mask_tau", "fb_refresh_mask_gamma",
+           "fb_block_attn", "fb_merge", "fb_step", "fb_step_noalloc", "fb_refresh_mask_tau",
+           "fb_refresh_mask_gamma",
            "fb_step_masked", "fb_append_block", "fb_select_chunks_ws", "fb_select_chunks",
            "fb_pool_chunk_keys", "fb_select_chunks_pooled",
            "fb_status_string", "fb_last_error", "fb_abi_version")
@@ -90,6 +91,9 @@ def lib() -> ctypes.CDLL:
         l.fb_step.argtypes = [D, P, P, P, P, P, S, P, P, P, P, P, P, i32, i32, i32, i32,
                               ctypes.POINTER(i32), P, sz, P]
         l.fb_step.restype = i32
+        l.fb_step_noalloc.argtypes = [D, P, P, P, P, P, S, P, P, P, P, P, P, i32, i32, i32, i32,
+                                      ctypes.POINTER(i32), P]
+        l.fb_step_noalloc.restype = i32
         f32 = ctypes.c_float
         l.fb_refresh_mask_tau.argtypes = [D, P, P, P, P, f32, i32, i32, P, P, P, sz, P]
         l.fb_refresh_mask_tau.restype = i32
@@ -229,6 +233,23 @@ def fb_step(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, sparse: Optional[Spar
                          _ptr(lse_res_cache), _ptr(o), _ptr(lse_out), step, refresh_period, mode,
                          int(bool(force_refresh)), ctypes.byref(refreshed), _ptr(ws), ws_bytes,
                          _stream(stream)), "fb_step")
+    return bool(refreshed.value)
+
+
+FB_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fb_step_noalloc(desc: Desc, q_blk, k_blk, v_blk, k_pre, v_pre, sparse: Optional[Sparse], o_ext_cache,
+                    lse_ext_cache, o_res_cache, lse_res_cache, o, lse_out, step: int, refresh_period: int,
+                    mode: int, force_refresh: bool, stream=None) -> bool:
+    """fb_step with the library's per-GPU scratch instead of a workspace; returns
+    True if this step refreshed the block-external cache."""
+    refreshed = ctypes.c_int32(0)
+    _check(lib().fb_step_noalloc(desc.ref, _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_pre), _ptr(v_pre),
+                                 _sref(sparse), _ptr(o_ext_cache), _ptr(lse_ext_cache), _ptr(o_res_cache),
+                                 _ptr(lse_res_cache), _ptr(o), _ptr(lse_out), step, refresh_period, mode,
+                                 int(bool(force_refresh)), ctypes.byref(refreshed), _stream(stream)),
+           "fb_step_noalloc")
     return bool(refreshed.value)
 
 

@@ -181,6 +181,27 @@ fb_status fb_step(const fb_desc* d, const void* q_blk, const void* k_blk, const 
                   int32_t refresh_period, int32_t mode, int32_t force_refresh,
                   int32_t* refreshed_out, void* ws, size_t ws_bytes, void* stream);
 
+/* fb_step without a workspace, for callers that cannot allocate device memory:
+ * code under graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments (less ws / ws_bytes), validation and results as
+ * fb_step.  The split-KV partials go to a scratch array of
+ * FB_NOALLOC_SCRATCH_BYTES that the library holds in the memory of every GPU
+ * it runs on, from the first use until the process ends; the call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  The array
+ * used is that of the calling thread's current device, which must be the
+ * device of `stream`.  A shape whose fb_workspace_size(d, sp) exceeds the
+ * scratch returns FB_ERR_WORKSPACE before anything is launched.  Every call on
+ * one GPU shares that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (several streams or threads in flight at once) race and
+ * give undefined results, so callers serialise them. */
+#define FB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fb_status fb_step_noalloc(const fb_desc* d, const void* q_blk, const void* k_blk,
+                          const void* v_blk, const void* k_pre, const void* v_pre,
+                          const fb_sparse* sp, float* o_ext_cache, float* lse_ext_cache,
+                          float* o_res_cache, float* lse_res_cache, void* o, float* lse_out,
+                          int32_t step, int32_t refresh_period, int32_t mode,
+                          int32_t force_refresh, int32_t* refreshed_out, void* stream);
+
 /* Adaptive reuse (explainer page, "Adaptive Reuse Strategies"): instead of a
  * fixed refresh period, decide per step and per (stream, KV head) whether the
  * block-external partial is recomputed, entirely on the device.  A mask is
