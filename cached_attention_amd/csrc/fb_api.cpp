@@ -1,7 +1,7 @@
 // Host side of libflashblock.so: argument validation, split planning and the
 // C ABI declared in include/flashblock.h.  Every check runs before anything is
 // enqueued; the library allocates nothing and keeps no state between calls.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -36,6 +36,11 @@ void clear_error() { g_err[0] = '\0'; }
 constexpr int kCUs = 256;
 constexpr int kMinSplitTiles = 4;  // >= 256 keys per split
 constexpr size_t kAlign = 256;
+// Launch limits: an attention grid of at most kMaxAttnWorkgroups workgroups of
+// up to 512 threads, and at most kMaxStreamHeads (stream, KV head) pairs, keep
+// every dispatch's work-item count inside its 32-bit limit.
+constexpr int64_t kMaxAttnWorkgroups = 1LL << 22;
+constexpr int64_t kMaxStreamHeads = 1LL << 21;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -95,6 +100,10 @@ fb_status check_desc(const fb_desc* d) {
     return fail(FB_ERR_SHAPE, "batch, hq, hkv and block_len must be >= 1 (got %d, %d, %d, %d)", d->batch,
                 d->hq, d->hkv, d->block_len);
   if (d->hq % d->hkv != 0) return fail(FB_ERR_SHAPE, "hq %d is not a multiple of hkv %d", d->hq, d->hkv);
+  // kernels with one workgroup per (stream, KV head) launch up to 1024 threads
+  // each: the grid's work-item count stays inside 32 bits
+  if ((int64_t)d->batch * d->hkv > kMaxStreamHeads)
+    return fail(FB_ERR_SHAPE, "batch * hkv = %lld > %lld", (long long)d->batch * d->hkv, (long long)kMaxStreamHeads);
   const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
   if (rows > (1LL << 30) || (int64_t)(d->hq / d->hkv) * d->block_len > (1 << 24))
     return fail(FB_ERR_SHAPE, "batch * hq * block_len too large");
@@ -191,7 +200,9 @@ fb_status plan_prefix(const fb_desc* d, int chunk_mode, int n_sel, int chunk_len
   for (int b = 0; b < d->batch; ++b)
     splits += ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel, p->chunk_tiles), st);
   const int64_t work = splits * units;
-  if (work > (1LL << 30)) return fail(FB_ERR_SHAPE, "prefix pass needs too many workgroups");
+  if (work > kMaxAttnWorkgroups)
+    return fail(FB_ERR_SHAPE, "prefix pass needs %lld workgroups > %lld", (long long)work,
+                (long long)kMaxAttnWorkgroups);
   p->total_splits = (int)splits;
   p->n_work = (int)work;
   p->grid = (int)ceil_div(work, 8) * 8;
@@ -300,6 +311,37 @@ fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const v
   return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream, head_mask);
 }
 
+// Workgroups of the block pass: (stream, KV head, row tile).
+int64_t block_work(const fb_desc* d, int cfg) {
+  const int64_t rows = (int64_t)(d->hq / d->hkv) * d->block_len;
+  return (int64_t)d->batch * d->hkv * ceil_div(rows, pass_info(d, cfg).rows);
+}
+
+// Every plan a call will launch, checked before anything is launched: the
+// prefix pass in the chunk modes it runs (dense, or both sparse modes), and
+// the block pass.
+fb_status check_plans(const fb_desc* d, const fb_sparse* sp, bool prefix, bool block) {
+  PrefixPlan p;
+  if (prefix) {
+    if (!sp) {
+      fb_status st = plan_prefix(d, fb::CHUNKS_ALL, 0, 64, &p);
+      if (st != FB_OK) return st;
+    } else {
+      for (int mode : {fb::CHUNKS_SELECTED, fb::CHUNKS_COMPLEMENT}) {
+        fb_status st = plan_prefix(d, mode, sp->k, sp->chunk_len, &p);
+        if (st != FB_OK) return st;
+      }
+    }
+  }
+  if (block) {
+    const int64_t work = block_work(d, block_cfg(d));
+    if (work > kMaxAttnWorkgroups)
+      return fail(FB_ERR_SHAPE, "block pass needs %lld workgroups > %lld", (long long)work,
+                  (long long)kMaxAttnWorkgroups);
+  }
+  return FB_OK;
+}
+
 fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const void* v_blk, const float* o_ext,
                     const float* lse_ext, void* o, float* lse_out, void* stream) {
   fb::AttnArgs a;
@@ -313,8 +355,7 @@ fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const vo
   const int cfg = block_cfg(d);
   a.row_tiles = (int)ceil_div(a.rows, pass_info(d, cfg).rows);
   a.split_tiles = (int)ceil_div(d->block_len, fb::kTile);
-  const int64_t work = (int64_t)d->batch * d->hkv * a.row_tiles;
-  if (work > (1LL << 30)) return fail(FB_ERR_SHAPE, "block pass needs too many workgroups");
+  const int64_t work = block_work(d, cfg);   // within kMaxAttnWorkgroups: check_plans ran first
   a.n_work = (int)work;
   a.grid = (int)ceil_div(work, 8) * 8;
   a.ext_o = o_ext;
@@ -349,114 +390,8 @@ fb_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 }  // namespace
 
-extern "C" {
-
-int32_t fb_abi_version(void) { return FB_ABI_VERSION; }
-
-const char* fb_last_error(void) { return g_err; }
-
-const char* fb_status_string(fb_status s) {
-  switch (s) {
-    case FB_OK: return "ok";
-    case FB_ERR_NULL: return "null pointer";
-    case FB_ERR_SHAPE: return "bad shape";
-    case FB_ERR_ALIGN: return "misaligned pointer or stride";
-    case FB_ERR_WORKSPACE: return "workspace too small";
-    case FB_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
-    case FB_ERR_ARG: return "bad argument";
-    case FB_ERR_HIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp) {
-  clear_error();
-  if (check_desc(d) != FB_OK || check_offsets(d) != FB_OK || check_sparse(sp, false) != FB_OK) return 0;
-  return workspace_for(d, sp);
-}
-
-fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
-                         const fb_sparse* sp, float* o_ext, float* lse_ext, void* ws, size_t ws_bytes,
-                         void* stream) {
-  clear_error();
-  fb_status st = check_desc(d);
-  if (st == FB_OK) st = check_offsets(d);
-  if (st == FB_OK) st = check_sparse(sp, true);
-  if (st != FB_OK) return st;
-  if (!q_blk || !o_ext || !lse_ext) return fail(FB_ERR_NULL, "q_blk, o_ext and lse_ext are required");
-  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
-    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
-  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre) || !aligned16(o_ext))
-    return fail(FB_ERR_ALIGN, "q_blk, k_pre, v_pre and o_ext must be 16-byte aligned");
-  const size_t need = workspace_for(d, sp);
-  st = check_ws(ws, ws_bytes, need);
-  if (st != FB_OK) return st;
-  const int mode = sp ? sp->mode : fb::CHUNKS_ALL;
-  return run_prefix(d, q_blk, k_pre, v_pre, mode, sp, nullptr, nullptr, o_ext, lse_ext, ws, ws_bytes, stream);
-}
-
-fb_status fb_prefix_partials(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
-                             const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream) {
-  clear_error();
-  fb_status st = check_desc(d);
-  if (st == FB_OK) st = check_offsets(d);
-  if (st == FB_OK) st = check_sparse(sp, true);
-  if (st != FB_OK) return st;
-  if (!q_blk) return fail(FB_ERR_NULL, "q_blk is required");
-  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
-    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
-  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre))
-    return fail(FB_ERR_ALIGN, "q_blk, k_pre and v_pre must be 16-byte aligned");
-  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
-  if (st != FB_OK) return st;
-  return run_partials(d, q_blk, k_pre, v_pre, sp ? sp->mode : fb::CHUNKS_ALL, sp, ws, ws_bytes, stream);
-}
-
-fb_status fb_prefix_combine(const fb_desc* d, const fb_sparse* sp, const float* extra_o, const float* extra_lse,
-                            float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes, void* stream) {
-  clear_error();
-  fb_status st = check_desc(d);
-  if (st == FB_OK) st = check_offsets(d);
-  if (st == FB_OK) st = check_sparse(sp, true);
-  if (st != FB_OK) return st;
-  if (!o_ext || !lse_ext) return fail(FB_ERR_NULL, "o_ext and lse_ext are required");
-  if ((extra_o == nullptr) != (extra_lse == nullptr))
-    return fail(FB_ERR_NULL, "extra_o and extra_lse must be both given or both NULL");
-  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
-  if (st != FB_OK) return st;
-  return run_combine(d, sp ? sp->mode : fb::CHUNKS_ALL, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes,
-                     stream);
-}
-
-fb_status fb_block_attn(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
-                        const float* o_ext, const float* lse_ext, void* o, float* lse_out, void* stream) {
-  clear_error();
-  fb_status st = check_desc(d);
-  if (st != FB_OK) return st;
-  if (!q_blk || !k_blk || !v_blk || !o) return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk and o are required");
-  if ((o_ext == nullptr) != (lse_ext == nullptr))
-    return fail(FB_ERR_NULL, "o_ext and lse_ext must be both given or both NULL");
-  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
-      (o_ext && !aligned16(o_ext)))
-    return fail(FB_ERR_ALIGN, "q_blk, k_blk, v_blk, o and o_ext must be 16-byte aligned");
-  return run_block(d, q_blk, k_blk, v_blk, o_ext, lse_ext, o, lse_out, stream);
-}
-
-fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a, const float* o_b,
-                   const float* lse_b, float* o, float* lse, void* stream) {
-  clear_error();
-  if (rows < 0 || rows > (1LL << 36)) return fail(FB_ERR_SHAPE, "rows = %lld out of range", (long long)rows);
-  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
-    return fail(FB_ERR_UNSUPPORTED, "head_dim %d must be a multiple of 4 in [4, 1024]", head_dim);
-  if (rows == 0) return FB_OK;
-  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return fail(FB_ERR_NULL, "fb_merge: NULL pointer");
-  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return fail(FB_ERR_ALIGN, "fb_merge: o_a, o_b, o must be 16-byte aligned");
-  return hip_status(fb::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, o, lse, stream), "merge launch");
-}
-
-}  // extern "C"
-
-// FB_DEBUG=1 in the environment turns on the reuse-step check below.
+// FB_DEBUG=1 in the environment turns on the checks below: a reuse step's cache
+// is scanned for NaN, and sparse chunk lists are checked against their contract.
 static bool debug_checks() {
   const char* e = getenv("FB_DEBUG");
   return e && e[0] == '1' && e[1] == '\0';
@@ -487,6 +422,146 @@ static fb_status cache_has_nan(const fb_desc* d, const float* oc, const float* l
   return FB_OK;
 }
 
+// Debug check of a sparse chunk list (ascending, unique, in range for its
+// stream), with the flag in the first word of the workspace; waits for the
+// answer on the stream.
+static fb_status chunk_list_bad(const fb_desc* d, const fb_sparse* sp, void* ws, void* stream) {
+  int32_t* flag = (int32_t*)ws;
+  int rc = fb::launch_chunk_check(sp->chunk_idx_dev, d->prefix_offsets_dev, d->batch, d->hkv, sp->k, sp->chunk_len,
+                                  flag, stream);
+  int32_t host = 0;
+  if (rc == 0) rc = (int)hipMemcpyAsync(&host, flag, sizeof(host), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (rc == 0) rc = (int)hipStreamSynchronize((hipStream_t)stream);
+  fb_status st = hip_status(rc, "FB_DEBUG chunk list check");
+  if (st != FB_OK) return st;
+  if (host)
+    return fail(FB_ERR_ARG, "fb_sparse.chunk_idx_dev: a (stream, KV head) list is not ascending and unique, or "
+                "names a chunk outside its stream's prefix");
+  return FB_OK;
+}
+
+static fb_status debug_chunk_check(const fb_desc* d, const fb_sparse* sp, void* ws, void* stream) {
+  if (!sp || !debug_checks() || capturing(stream)) return FB_OK;
+  return chunk_list_bad(d, sp, ws, stream);
+}
+
+extern "C" {
+
+int32_t fb_abi_version(void) { return FB_ABI_VERSION; }
+
+const char* fb_last_error(void) { return g_err; }
+
+const char* fb_status_string(fb_status s) {
+  switch (s) {
+    case FB_OK: return "ok";
+    case FB_ERR_NULL: return "null pointer";
+    case FB_ERR_SHAPE: return "bad shape";
+    case FB_ERR_ALIGN: return "misaligned pointer or stride";
+    case FB_ERR_WORKSPACE: return "workspace too small";
+    case FB_ERR_UNSUPPORTED: return "unsupported dtype or head_dim";
+    case FB_ERR_ARG: return "bad argument";
+    case FB_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t fb_workspace_size(const fb_desc* d, const fb_sparse* sp) {
+  clear_error();
+  if (check_desc(d) != FB_OK || check_offsets(d) != FB_OK || check_sparse(sp, false) != FB_OK ||
+      check_plans(d, sp, true, false) != FB_OK)
+    return 0;
+  return workspace_for(d, sp);
+}
+
+fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
+                         const fb_sparse* sp, float* o_ext, float* lse_ext, void* ws, size_t ws_bytes,
+                         void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st == FB_OK) st = check_plans(d, sp, true, false);
+  if (st != FB_OK) return st;
+  if (!q_blk || !o_ext || !lse_ext) return fail(FB_ERR_NULL, "q_blk, o_ext and lse_ext are required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre) || !aligned16(o_ext))
+    return fail(FB_ERR_ALIGN, "q_blk, k_pre, v_pre and o_ext must be 16-byte aligned");
+  const size_t need = workspace_for(d, sp);
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FB_OK) return st;
+  st = debug_chunk_check(d, sp, ws, stream);
+  if (st != FB_OK) return st;
+  const int mode = sp ? sp->mode : fb::CHUNKS_ALL;
+  return run_prefix(d, q_blk, k_pre, v_pre, mode, sp, nullptr, nullptr, o_ext, lse_ext, ws, ws_bytes, stream);
+}
+
+fb_status fb_prefix_partials(const fb_desc* d, const void* q_blk, const void* k_pre, const void* v_pre,
+                             const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st == FB_OK) st = check_plans(d, sp, true, false);
+  if (st != FB_OK) return st;
+  if (!q_blk) return fail(FB_ERR_NULL, "q_blk is required");
+  if (total_prefix(d) > 0 && (!k_pre || !v_pre))
+    return fail(FB_ERR_NULL, "k_pre and v_pre are required for a non-empty prefix");
+  if (!aligned16(q_blk) || !aligned16(k_pre) || !aligned16(v_pre))
+    return fail(FB_ERR_ALIGN, "q_blk, k_pre and v_pre must be 16-byte aligned");
+  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
+  if (st == FB_OK) st = debug_chunk_check(d, sp, ws, stream);
+  if (st != FB_OK) return st;
+  return run_partials(d, q_blk, k_pre, v_pre, sp ? sp->mode : fb::CHUNKS_ALL, sp, ws, ws_bytes, stream);
+}
+
+fb_status fb_prefix_combine(const fb_desc* d, const fb_sparse* sp, const float* extra_o, const float* extra_lse,
+                            float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_sparse(sp, true);
+  if (st == FB_OK) st = check_plans(d, sp, true, false);
+  if (st != FB_OK) return st;
+  if (!o_ext || !lse_ext) return fail(FB_ERR_NULL, "o_ext and lse_ext are required");
+  if ((extra_o == nullptr) != (extra_lse == nullptr))
+    return fail(FB_ERR_NULL, "extra_o and extra_lse must be both given or both NULL");
+  st = check_ws(ws, ws_bytes, workspace_for(d, sp));
+  if (st != FB_OK) return st;
+  return run_combine(d, sp ? sp->mode : fb::CHUNKS_ALL, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes,
+                     stream);
+}
+
+fb_status fb_block_attn(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
+                        const float* o_ext, const float* lse_ext, void* o, float* lse_out, void* stream) {
+  clear_error();
+  fb_status st = check_desc(d);
+  if (st == FB_OK) st = check_plans(d, nullptr, false, true);
+  if (st != FB_OK) return st;
+  if (!q_blk || !k_blk || !v_blk || !o) return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk and o are required");
+  if ((o_ext == nullptr) != (lse_ext == nullptr))
+    return fail(FB_ERR_NULL, "o_ext and lse_ext must be both given or both NULL");
+  if (!aligned16(q_blk) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o) ||
+      (o_ext && !aligned16(o_ext)))
+    return fail(FB_ERR_ALIGN, "q_blk, k_blk, v_blk, o and o_ext must be 16-byte aligned");
+  return run_block(d, q_blk, k_blk, v_blk, o_ext, lse_ext, o, lse_out, stream);
+}
+
+fb_status fb_merge(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a, const float* o_b,
+                   const float* lse_b, float* o, float* lse, void* stream) {
+  clear_error();
+  if (rows < 0 || rows > (1LL << 36)) return fail(FB_ERR_SHAPE, "rows = %lld out of range", (long long)rows);
+  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
+    return fail(FB_ERR_UNSUPPORTED, "head_dim %d must be a multiple of 4 in [4, 1024]", head_dim);
+  if (rows == 0) return FB_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return fail(FB_ERR_NULL, "fb_merge: NULL pointer");
+  if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return fail(FB_ERR_ALIGN, "fb_merge: o_a, o_b, o must be 16-byte aligned");
+  return hip_status(fb::launch_merge(rows, head_dim, o_a, lse_a, o_b, lse_b, o, lse, stream), "merge launch");
+}
+
+}  // extern "C"
+
+
 // Argument checks of fb_step and fb_step_noalloc (everything but the
 // workspace); *need receives the workspace the step uses.
 static fb_status step_checks(const fb_desc* d, const void* q_blk, const void* k_blk, const void* v_blk,
@@ -496,6 +571,7 @@ static fb_status step_checks(const fb_desc* d, const void* q_blk, const void* k_
   fb_status st = check_desc(d);
   if (st == FB_OK) st = check_offsets(d);
   if (st == FB_OK) st = check_sparse(sp, false);
+  if (st == FB_OK) st = check_plans(d, sp, true, true);
   if (st != FB_OK) return st;
   if (step < 0) return fail(FB_ERR_ARG, "step = %d < 0", step);
   if (refresh_period < 1) return fail(FB_ERR_ARG, "refresh_period = %d < 1", refresh_period);
@@ -521,6 +597,8 @@ static fb_status step_run(const fb_desc* d, const void* q_blk, const void* k_blk
                           int32_t* refreshed_out, void* ws, size_t ws_bytes, void* stream) {
   fb_status st = FB_OK;
   const bool refresh = mode == FB_MODE_FULL || force_refresh != 0 || step % refresh_period == 0;
+  st = debug_chunk_check(d, sp, ws, stream);
+  if (st != FB_OK) return st;
   if (refreshed_out) *refreshed_out = refresh ? 1 : 0;
   if (!refresh && debug_checks() && !capturing(stream)) {
     // the partial this step reuses: the block-external cache, or the residual in the sparse variant
@@ -659,6 +737,7 @@ fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk,
   clear_error();
   fb_status st = check_desc(d);
   if (st == FB_OK) st = check_offsets(d);
+  if (st == FB_OK) st = check_plans(d, nullptr, true, true);
   if (st != FB_OK) return st;
   if (!q_blk || !k_blk || !v_blk || !mask || !o_ext_cache || !lse_ext_cache || !o)
     return fail(FB_ERR_NULL, "q_blk, k_blk, v_blk, mask, o_ext_cache, lse_ext_cache and o are required");
@@ -720,7 +799,8 @@ static fb_status chunk_geometry(const fb_desc* d, int32_t chunk_len, int32_t* n_
     hi = std::max(hi, n);
     lo = std::min(lo, n);
   }
-  if (hi * d->batch * d->hkv > (1LL << 30)) return fail(FB_ERR_SHAPE, "too many chunks");
+  // the scoring grid has one workgroup per 64 chunks of every (stream, KV head)
+  if (hi * d->batch * d->hkv > (1LL << 26)) return fail(FB_ERR_SHAPE, "too many chunks");
   *n_max = (int32_t)hi;
   *n_min = (int32_t)lo;
   return FB_OK;

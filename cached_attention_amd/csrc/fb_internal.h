@@ -180,6 +180,10 @@ int launch_select_pooled(const SelectArgs& a, void* stream);
 int launch_gamma(const GammaArgs& g, void* stream);
 // *flag = 1 if any of x[0..n) is NaN (flag cleared first when clear is set)
 int launch_nan_scan(const float* x, int64_t n, int32_t* flag, bool clear, void* stream);
+// *flag = 1 unless every [B][Hkv][k] chunk list is strictly ascending and in
+// range for its stream (flag cleared first)
+int launch_chunk_check(const int32_t* list, const int64_t* offsets, int32_t B, int32_t Hkv, int32_t k,
+                       int32_t chunk_len, int32_t* flag, void* stream);
 
 // Scratch of the no-allocation step: a file-scope device array of this many
 // bytes in fb_kernels.hip, one per GPU.  *ptr receives its address on the

@@ -924,11 +924,19 @@ __global__ void __launch_bounds__(256) attn_f32m(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int D>
+__device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, int lane);
+
+// one wave per row; the grid strides over the rows (capped grid)
+template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64_t rows) {
-  constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
+    combine_row<D>(c, row, lane);
+}
+
+template <int D>
+__device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, int lane) {
+  constexpr int PER = D / 64;
   const int64_t hl = (int64_t)c.Hq * c.Lb;
   const int b = (int)(row / hl);
   const int64_t rem = row % hl;
@@ -1004,11 +1012,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64
 // two-partial merge: one wave per row (all reads of a row precede its writes)
 // ---------------------------------------------------------------------------
 
+__device__ __forceinline__ void merge_row(int64_t row, int D, const float* oa, const float* la, const float* ob,
+                                          const float* lb, float* o, float* lse, int lane);
+
+// one wave per row; the grid strides over the rows (capped grid)
 __global__ void __launch_bounds__(256) merge_kernel(int64_t rows, int D, const float* oa, const float* la,
                                                     const float* ob, const float* lb, float* o, float* lse) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (int64_t)gridDim.x * 4)
+    merge_row(row, D, oa, la, ob, lb, o, lse, lane);
+}
+
+__device__ __forceinline__ void merge_row(int64_t row, int D, const float* oa, const float* la, const float* ob,
+                                          const float* lb, float* o, float* lse, int lane) {
   const float l1 = la[row], l2 = lb[row];
   const float mm = fmaxf(l1, l2);
   const bool empty = mm == kNegInf;
@@ -1040,10 +1056,17 @@ __device__ __forceinline__ float ld_elem(const void* p, int64_t i, int dtype) {
 
 // threshold-based reuse, part 1: one wave per block token -- did its K or V
 // row (any KV head, any dim) change by more than eps since the previous step?
+__device__ __forceinline__ void tau_flag_token(const TauArgs& t, int64_t tok, int lane);
+
+// one wave per token; the grid strides over the tokens (capped grid)
 __global__ void __launch_bounds__(256) tau_flags_kernel(const TauArgs t) {
   const int lane = threadIdx.x & 63;
-  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= (int64_t)t.B * t.Lb) return;
+  const int64_t toks = (int64_t)t.B * t.Lb;
+  for (int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tok < toks; tok += (int64_t)gridDim.x * 4)
+    tau_flag_token(t, tok, lane);
+}
+
+__device__ __forceinline__ void tau_flag_token(const TauArgs& t, int64_t tok, int lane) {
   if (t.step == 0) {   // no previous step: every token is new
     if (lane == 0) t.flags[tok] = 1;
     return;
@@ -1185,8 +1208,8 @@ __global__ void __launch_bounds__(1024) gamma_kernel(const GammaArgs a) {
 __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
   const int pieces = a.D * a.esize / 16;   // 16-byte pieces per (token, KV head) row
   const int64_t per_tensor = (int64_t)a.B * a.Lb * a.Hkv * pieces;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= 2 * per_tensor) return;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < 2 * per_tensor; j += (int64_t)gridDim.x * 256) {
+  int64_t i = j;
   const bool is_v = i >= per_tensor;
   if (is_v) i -= per_tensor;
   const int pc = (int)(i % pieces);
@@ -1200,6 +1223,7 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendArgs a) {
   const char* s = (const char*)(is_v ? a.v_blk : a.k_blk) + src * a.esize + pc * 16;
   char* d = (char*)(is_v ? a.v_pre : a.k_pre) + dst * a.esize + pc * 16;
   *(f32x4*)d = *(const f32x4*)s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1265,17 +1289,18 @@ __device__ __forceinline__ void pool_chunk(const SelectArgs& a, int b, int c, in
 // grid: 4 waves per workgroup over (stream, chunk first_chunk.., KV head)
 __global__ void __launch_bounds__(256) pool_kernel(const SelectArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int span = a.max_chunks - a.first_chunk;
-  if (w >= (int64_t)a.B * span * a.Hkv) return;
-  const int g = (int)(w % a.Hkv);
-  const int64_t r = w / a.Hkv;
-  const int c = a.first_chunk + (int)(r % span), b = (int)(r / span);
-  if (c >= chunks_of(a.offsets, b, a.chunk_len)) return;
-  if (a.dtype == kDtypeBf16) {
-    if (a.D == 128) pool_chunk<128, __bf16>(a, b, c, g, lane); else pool_chunk<64, __bf16>(a, b, c, g, lane);
-  } else {
-    if (a.D == 128) pool_chunk<128, float>(a, b, c, g, lane); else pool_chunk<64, float>(a, b, c, g, lane);
+  const int64_t n = (int64_t)a.B * span * a.Hkv;
+  for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < n; w += (int64_t)gridDim.x * 4) {
+    const int g = (int)(w % a.Hkv);
+    const int64_t r = w / a.Hkv;
+    const int c = a.first_chunk + (int)(r % span), b = (int)(r / span);
+    if (c >= chunks_of(a.offsets, b, a.chunk_len)) continue;   // wave-uniform
+    if (a.dtype == kDtypeBf16) {
+      if (a.D == 128) pool_chunk<128, __bf16>(a, b, c, g, lane); else pool_chunk<64, __bf16>(a, b, c, g, lane);
+    } else {
+      if (a.D == 128) pool_chunk<128, float>(a, b, c, g, lane); else pool_chunk<64, float>(a, b, c, g, lane);
+    }
   }
 }
 
@@ -1553,6 +1578,22 @@ __global__ void __launch_bounds__(256) nan_scan_kernel(const float* x, int64_t n
   if (bad) *flag = 1;
 }
 
+// debug check of a sparse chunk list [B][Hkv][k]: *flag = 1 unless every
+// (stream, KV head) list is strictly ascending with 0 <= c < the stream's
+// chunk count (the flag is cleared first)
+__global__ void __launch_bounds__(256) chunk_check_kernel(const int32_t* list, const int64_t* offsets, int32_t B,
+                                                          int32_t Hkv, int32_t k, int32_t chunk_len, int32_t* flag) {
+  bool bad = false;
+  const int64_t n = (int64_t)B * Hkv * k;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int b = (int)(i / ((int64_t)Hkv * k));
+    const int j = (int)(i % k);
+    const int32_t c = list[i];
+    bad |= c < 0 || c >= chunks_of(offsets, b, chunk_len) || (j > 0 && list[i - 1] >= c);
+  }
+  if (bad) *flag = 1;
+}
+
 // ---------------------------------------------------------------------------
 // scratch of the no-allocation step (fb_step_noalloc)
 // ---------------------------------------------------------------------------
@@ -1589,6 +1630,12 @@ int noalloc_scratch(void** ptr) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+
+// 1-D grids of the row/element kernels are capped, and those kernels stride
+// over what the grid does not cover: a dispatch's work-item count stays far
+// inside its 32-bit limit for any size the host accepts.
+constexpr int64_t kMaxBlocks = 1 << 20;
+static dim3 capped_grid(int64_t blocks) { return dim3((unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks)); }
 
 template <int D, int QT, int NW, int NS, int WPC, bool P, int RW>
 static int launch_bf16(const AttnArgs& a, hipStream_t s) {
@@ -1627,7 +1674,7 @@ int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partia
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const dim3 grid = capped_grid((rows + 3) / 4);
   if (c.D == 64)
     hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, s, c, rows);
   else
@@ -1639,7 +1686,7 @@ int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* l
                  const float* lb, float* o, float* lse, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows, head_dim, oa, la,
+  hipLaunchKernelGGL(merge_kernel, capped_grid((rows + 3) / 4), dim3(256), 0, s, rows, head_dim, oa, la,
                      ob, lb, o, lse);
   return (int)hipGetLastError();
 }
@@ -1647,21 +1694,21 @@ int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* l
 int launch_tau(const TauArgs& t, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t toks = (int64_t)t.B * t.Lb;
-  hipLaunchKernelGGL(tau_flags_kernel, dim3((unsigned)((toks + 3) / 4)), dim3(256), 0, s, t);
+  hipLaunchKernelGGL(tau_flags_kernel, capped_grid((toks + 3) / 4), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tau_finalize_kernel, dim3((unsigned)t.B), dim3(256), 0, s, t);
   return (int)hipGetLastError();
 }
 
 int launch_append(const AppendArgs& a, void* stream) {
   const int64_t n = 2LL * a.B * a.Lb * a.Hkv * (a.D * a.esize / 16);
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(append_kernel, capped_grid((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_pool(const SelectArgs& a, void* stream) {
   const int64_t waves = (int64_t)a.B * (a.max_chunks - a.first_chunk) * a.Hkv;
   if (waves <= 0) return 0;
-  hipLaunchKernelGGL(pool_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(pool_kernel, capped_grid((waves + 3) / 4), dim3(256), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
@@ -1685,6 +1732,17 @@ int launch_nan_scan(const float* x, int64_t n, int32_t* flag, bool clear, void* 
     const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
     hipLaunchKernelGGL(nan_scan_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, flag);
   }
+  return (int)hipGetLastError();
+}
+
+int launch_chunk_check(const int32_t* list, const int64_t* offsets, int32_t B, int32_t Hkv, int32_t k,
+                       int32_t chunk_len, int32_t* flag, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(flag_clear_kernel, dim3(1), dim3(64), 0, s, flag);
+  const int64_t n = (int64_t)B * Hkv * k;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  hipLaunchKernelGGL(chunk_check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, list, offsets, B, Hkv, k,
+                     chunk_len, flag);
   return (int)hipGetLastError();
 }
 

@@ -44,7 +44,10 @@
  *
  * Errors.  Arguments are validated before anything is enqueued: on an error
  * nothing is launched, outputs are untouched, the status code says which check
- * failed and fb_last_error() (thread-local) gives the detail.  A launch failure
+ * failed and fb_last_error() (thread-local) gives the detail.  Size limits:
+ * batch * hkv <= 2^21, batch * hq * block_len <= 2^30, and each attention pass
+ * at most 2^22 workgroups (FB_ERR_SHAPE beyond them), so that every launch's
+ * grid stays inside the dispatch limits.  A launch failure
  * returns FB_ERR_HIP.  Faults inside a kernel surface at the caller's next
  * synchronisation.  No C++ exception crosses this interface.
  */
@@ -98,7 +101,13 @@ typedef struct fb_desc {
  * tokens (the last one of a stream may be shorter); for each (stream, KV head)
  * `k` chunk indices are listed, ascending and unique, each < ceil(Lp_b/chunk_len).
  * SELECTED attends to the listed chunks only, COMPLEMENT to every other prefix
- * token (the unselected keys whose contribution is cached as the residual). */
+ * token (the unselected keys whose contribution is cached as the residual).
+ * The kernels do not check the lists (an index outside the stream selects
+ * nothing); with FB_DEBUG=1 in the environment, fb_step, fb_step_noalloc,
+ * fb_prefix_attn and fb_prefix_partials check them on the device first (the
+ * flag in the first word of the workspace, waiting on the stream; skipped
+ * while the stream is being captured) and return FB_ERR_ARG before launching
+ * anything else if a list breaks this contract. */
 typedef struct fb_sparse {
   const int32_t* chunk_idx_dev; /* [B][Hkv][k] int32, device */
   int32_t k;                    /* chunks listed per (stream, KV head), >= 1 */

@@ -68,3 +68,32 @@ def test_debug_check_is_skipped_under_graph_capture(monkeypatch):
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(st.o, ref)
+
+
+@pytest.mark.parametrize("bad", [[[3, 3], [0, 9]], [[4, 1], [0, 9]], [[1, 10], [0, 9]], [[-1, 4], [0, 9]]],
+                         ids=["duplicate", "unsorted", "past_the_end", "negative"])
+def test_debug_check_refuses_bad_chunk_list(monkeypatch, bad):
+    """FB_DEBUG=1: a sparse step, and a sparse prefix pass, refuse a chunk list
+    that is not ascending and unique within its stream's 10 chunks, before
+    launching anything; a valid list passes."""
+    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=640, hq=8, hkv=2, block_len=16)
+    prefix, blocks = wl.make_inputs(w)
+    blk = blocks[0]
+    st = AttentionStep("bf16", w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets,
+                       chunks=torch.tensor([bad], dtype=torch.int32))
+    kp, vp = dev(prefix.k), dev(prefix.v)
+    q, k, v = dev(blk.q[0]), dev(blk.k[0]), dev(blk.v[0])
+    monkeypatch.setenv("FB_DEBUG", "1")
+    st.o.fill_(7.0)
+    with pytest.raises(fbl.FlashBlockError) as e:
+        st.step(q, k, v, kp, vp, 0, 8)
+    assert e.value.status == fbl.FB_ERR_ARG and "ascending" in fbl.fb_last_error()
+    with pytest.raises(fbl.FlashBlockError) as e:
+        st.prefix(q, kp, vp, fbl.FB_CHUNKS_SELECTED)
+    assert e.value.status == fbl.FB_ERR_ARG
+    torch.cuda.synchronize()
+    assert bool((st.o.float() == 7.0).all())   # nothing ran
+    st.chunks.copy_(torch.tensor([[[1, 4], [0, 9]]], dtype=torch.int32))
+    st.step(q, k, v, kp, vp, 0, 8)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st.o.float()).all()
