@@ -241,7 +241,7 @@ fb_status hip_status(int err, const char* what) {
 // same plan (and so the same workspace layout) from (d, chunk mode, sp).
 fb_status run_partials(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
                        const fb_sparse* sp, void* ws, size_t ws_bytes, void* stream,
-                       const int32_t* head_mask = nullptr) {
+                       const int32_t* unit_plan = nullptr) {
   PrefixPlan p;
   const int n_sel = sp ? sp->k : 0;
   fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
@@ -265,13 +265,13 @@ fb_status run_partials(const fb_desc* d, const void* q, const void* k_pre, const
   a.chunk_mode = chunk_mode;
   a.part_o = (float*)ws;
   a.part_lse = (float*)((char*)ws + p.part_o_bytes);
-  a.head_mask = head_mask;
+  a.plan = unit_plan;
   return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, p.cfg, true, stream), "prefix attention launch");
 }
 
 fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, const float* extra_o,
                       const float* extra_lse, float* o_ext, float* lse_ext, const void* ws, size_t ws_bytes,
-                      void* stream, const int32_t* head_mask = nullptr) {
+                      void* stream, const int32_t* unit_plan = nullptr) {
   PrefixPlan p;
   const int n_sel = sp ? sp->k : 0;
   fb_status st = plan_prefix(d, chunk_mode, n_sel, sp ? sp->chunk_len : 64, &p);
@@ -296,7 +296,9 @@ fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, con
   c.extra_lse = extra_lse;
   c.o = o_ext;
   c.lse = lse_ext;
-  c.head_mask = head_mask;
+  c.plan = unit_plan;
+  // a unit plan packs G * Lb rows per unit: the workspace holds Hkv units per split of the all-heads plan
+  if (unit_plan) c.total_splits = p.total_splits * d->hkv;
   c.Hkv = d->hkv;
   c.G = d->hq / d->hkv;
   const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
@@ -305,10 +307,10 @@ fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, con
 
 fb_status run_prefix(const fb_desc* d, const void* q, const void* k_pre, const void* v_pre, int chunk_mode,
                      const fb_sparse* sp, const float* extra_o, const float* extra_lse, float* o_ext,
-                     float* lse_ext, void* ws, size_t ws_bytes, void* stream, const int32_t* head_mask = nullptr) {
-  fb_status st = run_partials(d, q, k_pre, v_pre, chunk_mode, sp, ws, ws_bytes, stream, head_mask);
+                     float* lse_ext, void* ws, size_t ws_bytes, void* stream, const int32_t* unit_plan = nullptr) {
+  fb_status st = run_partials(d, q, k_pre, v_pre, chunk_mode, sp, ws, ws_bytes, stream, unit_plan);
   if (st != FB_OK) return st;
-  return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream, head_mask);
+  return run_combine(d, chunk_mode, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes, stream, unit_plan);
 }
 
 // Workgroups of the block pass: (stream, KV head, row tile).
@@ -365,12 +367,15 @@ fb_status run_block(const fb_desc* d, const void* q, const void* k_blk, const vo
   return hip_status(fb::launch_attn(a, d->dtype, d->head_dim, cfg, false, stream), "block attention launch");
 }
 
+// Bytes of a masked step's unit plan, kept after the all-heads plan's partials.
+size_t unit_plan_bytes(const fb_desc* d) { return align_up((size_t)fb::plan_ints((int64_t)d->batch * d->hkv) * 4); }
+
 size_t workspace_for(const fb_desc* d, const fb_sparse* sp) {
   PrefixPlan p;
   size_t need = 0;
   if (!sp) {
     if (plan_prefix(d, fb::CHUNKS_ALL, 0, 64, &p) != FB_OK) return 0;
-    need = p.part_o_bytes + p.part_lse_bytes;
+    need = p.part_o_bytes + p.part_lse_bytes + unit_plan_bytes(d);   // fb_step_masked: partials + plan
   } else {
     for (int mode : {fb::CHUNKS_SELECTED, fb::CHUNKS_COMPLEMENT}) {
       if (plan_prefix(d, mode, sp->k, sp->chunk_len, &p) != FB_OK) return 0;
@@ -748,8 +753,24 @@ fb_status fb_step_masked(const fb_desc* d, const void* q_blk, const void* k_blk,
     return fail(FB_ERR_ALIGN, "all tensor base pointers must be 16-byte aligned");
   st = check_ws(ws, ws_bytes, workspace_for(d, nullptr));
   if (st != FB_OK) return st;
+  // the unit plan of the pairs the mask recomputes, after the partials
+  PrefixPlan p;
+  st = plan_prefix(d, fb::CHUNKS_ALL, 0, 64, &p);
+  if (st != FB_OK) return st;
+  fb::UnitPlanArgs u;
+  memset(&u, 0, sizeof(u));
+  u.mask = mask;
+  u.offsets = d->prefix_offsets_dev;
+  u.B = d->batch;
+  u.Hkv = d->hkv;
+  u.row_tiles = p.row_tiles;
+  u.min_split = d->dtype == FB_F32 ? 1 : kMinSplitTiles;
+  u.cap = p.n_work;
+  u.plan = (int32_t*)((char*)ws + p.part_o_bytes + p.part_lse_bytes);
+  st = hip_status(fb::launch_unit_plan(u, stream), "unit plan launch");
+  if (st != FB_OK) return st;
   st = run_prefix(d, q_blk, k_pre, v_pre, fb::CHUNKS_ALL, nullptr, nullptr, nullptr, o_ext_cache, lse_ext_cache,
-                  ws, ws_bytes, stream, mask);
+                  ws, ws_bytes, stream, u.plan);
   if (st != FB_OK) return st;
   return run_block(d, q_blk, k_blk, v_blk, o_ext_cache, lse_ext_cache, o, lse_out, stream);
 }

@@ -96,9 +96,10 @@ struct AttnArgs {
   const float* ext_lse;
   void* o;
   float* lse_out;
-  // per-(stream, KV head) recompute mask [B][Hkv] (nullable = all): workgroups
-  // of a masked-out head exit at once
-  const int32_t* head_mask;
+  // unit plan of a masked step (nullable = every (stream, KV head)): the
+  // workgroups map onto the listed (stream, KV head) pairs only, and the
+  // partials are packed per listed pair (layout below)
+  const int32_t* plan;
 };
 
 struct CombineArgs {
@@ -112,9 +113,27 @@ struct CombineArgs {
   const float* extra_lse;
   float* o;                // [B][Hq][Lb][D]
   float* lse;              // [B][Hq][Lb]
-  const int32_t* head_mask;  // [B][Hkv] (nullable = all): rows of masked-out heads are left untouched
+  const int32_t* plan;     // unit plan (nullable = every head): rows of unlisted heads are left untouched
   int32_t Hkv, G;
 };
+
+// Unit plan of a masked step, int32 in device memory, written by
+// launch_unit_plan from a [B][Hkv] recompute mask (P = B * Hkv pairs):
+//   [0] workgroups with work (units * row tiles)   [1] tiles per split
+//   [2] listed pairs n                              [3] units (splits of all listed pairs)
+//   [4 .. 4+P)       pair b * Hkv + g of listed pair a (a < n), in mask order
+//   [4+P .. 5+2P)    first unit of listed pair a (a <= n; [n] = units)
+//   [5+2P .. 5+3P)   listed index of pair b * Hkv + g, or -1
+// Unit u holds G * Lb partial rows (query head of the group, block position).
+inline int64_t plan_ints(int64_t pairs) { return 5 + 3 * pairs; }
+struct UnitPlanArgs {
+  const int32_t* mask;      // [B][Hkv], nonzero = recompute
+  const int64_t* offsets;   // device prefix offsets [B+1]
+  int32_t B, Hkv, row_tiles, min_split;
+  int32_t cap;              // at most this many workgroups (the all-heads plan's)
+  int32_t* plan;
+};
+int launch_unit_plan(const UnitPlanArgs& u, void* stream);
 
 // Adaptive reuse masks.
 struct TauArgs {

@@ -130,6 +130,7 @@ __device__ __forceinline__ bool next_tile(TileIter& it, int64_t& tok0, int& nval
 // XCD's L2.  Then finds the stream b and the logical-tile range of the split.
 struct Work {
   int x, g, rt, b;
+  int hs, h_off;   // partial row of query head h: (x * hs + h_off + h - g * G) * Lb + position
   TileIter it;
   const char* kbase;
   const char* vbase;
@@ -140,11 +141,6 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
   const int L = blockIdx.x;
   const int per = a.grid >> 3;
   const int w = (L & 7) * per + (L >> 3);
-  if (w >= a.n_work) return false;
-  wk.rt = w % a.row_tiles;
-  const int gx = w / a.row_tiles;
-  wk.g = gx % a.Hkv;
-  wk.x = gx / a.Hkv;
   TileIter& it = wk.it;
   it.list = nullptr;
   it.nlist = 0;
@@ -152,6 +148,44 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
   it.mode = CHUNKS_ALL;
   it.ct = 1;
   int64_t tok_base;
+  wk.hs = a.Hq;
+  if (a.offsets && a.plan) {
+    // masked step: unit u = w / row_tiles is split j of the listed pair that
+    // holds it (the last pair whose first unit is <= u)
+    const int32_t* pl = a.plan;
+    if (w >= ld_const(pl, 0)) return false;
+    const int st = ld_const(pl, 1), n = ld_const(pl, 2);
+    const int P = a.B * a.Hkv;
+    const int32_t* base = pl + 4 + P;
+    wk.rt = w % a.row_tiles;
+    const int u = w / a.row_tiles;
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ld_const(base, mid) <= u) lo = mid; else hi = mid - 1;
+    }
+    const int bg = ld_const(pl + 4, lo);
+    wk.b = bg / a.Hkv;
+    wk.g = bg % a.Hkv;
+    wk.x = u;
+    wk.hs = a.G;   // units hold only their group's query heads
+    wk.h_off = 0;
+    const int j = u - ld_const(base, lo);
+    it.lp = prefix_len(a.offsets, wk.b);
+    const int nl = (int)((it.lp + kTile - 1) / kTile);
+    it.lt = j * st;
+    it.lt_end = min(nl, it.lt + st);
+    tok_base = ld_const(a.offsets, wk.b);
+    wk.kbase = (const char*)a.k + (tok_base * a.kv_st + (int64_t)wk.g * a.kv_sh) * ESZ;
+    wk.vbase = (const char*)a.v + (tok_base * a.kv_st + (int64_t)wk.g * a.kv_sh) * ESZ;
+    return true;
+  }
+  if (w >= a.n_work) return false;
+  wk.rt = w % a.row_tiles;
+  const int gx = w / a.row_tiles;
+  wk.g = gx % a.Hkv;
+  wk.x = gx / a.Hkv;
+  wk.h_off = wk.g * a.G;
   if (a.offsets) {
     int acc = 0, b = 0, j = 0;
     for (; b < a.B; ++b) {
@@ -348,7 +382,6 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 
   Work wk;
   if (!decode_work<2>(a, wk)) return;
-  if (a.head_mask && ld_const(a.head_mask, (int64_t)wk.b * a.Hkv + wk.g) == 0) return;   // cache reused
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -723,7 +756,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     const float inv = any ? 1.f / lt : 0.f;
     const float lse = any ? (m_run[qt] + __log2f(lt)) * kLn2 : kNegInf;
     if constexpr (PARTIAL) {
-      const int64_t prow = ((int64_t)wk.x * a.Hq + h) * a.Lb + pos;
+      const int64_t prow = ((int64_t)wk.x * wk.hs + wk.h_off + row / a.Lb) * a.Lb + pos;
       float* po = a.part_o + prow * D + 4 * lg;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) *(f32x4*)(po + dt * 16) = oacc[dt][qt] * inv;
@@ -783,7 +816,6 @@ __global__ void __launch_bounds__(256) attn_f32m(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Vs[kTile * LDK];
   Work wk;
   if (!decode_work<4>(a, wk)) return;
-  if (a.head_mask && ld_const(a.head_mask, (int64_t)wk.b * a.Hkv + wk.g) == 0) return;   // cache reused
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -890,7 +922,7 @@ __global__ void __launch_bounds__(256) attn_f32m(const AttnArgs a) {
   const float lse = any ? (m_run + __log2f(l)) * kLn2 : kNegInf;
   // lane (l16, lg) holds O^T rows 4*lg + i of every d tile: dims (4*lg + i)*DT + dt
   if constexpr (PARTIAL) {
-    const int64_t prow = ((int64_t)wk.x * a.Hq + h) * a.Lb + pos;
+    const int64_t prow = ((int64_t)wk.x * wk.hs + wk.h_off + row / a.Lb) * a.Lb + pos;
     float* po = a.part_o + prow * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -937,13 +969,25 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64
 template <int D>
 __device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, int lane) {
   constexpr int PER = D / 64;
-  const int64_t hl = (int64_t)c.Hq * c.Lb;
-  const int b = (int)(row / hl);
-  const int64_t rem = row % hl;
-  if (c.head_mask && ld_const(c.head_mask, (int64_t)b * c.Hkv + (int)(rem / c.Lb) / c.G) == 0) return;
-  int x0 = 0;
-  for (int bb = 0; bb < b; ++bb) x0 += splits_of(c.offsets, bb, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
-  int ns = splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
+  const int64_t hl_out = (int64_t)c.Hq * c.Lb;
+  const int b = (int)(row / hl_out);
+  // partial rows of this output row: split x of its run is (x0 + x) * hl + rem
+  int64_t hl = hl_out, rem = row % hl_out;
+  int x0 = 0, ns = 0;
+  if (c.plan) {   // masked step: only the listed pairs, each unit holding its group's G * Lb rows
+    const int P = c.B * c.Hkv;
+    const int h = (int)(rem / c.Lb), pos = (int)(rem % c.Lb);
+    const int a = ld_const(c.plan + 5 + 2 * P, (int64_t)b * c.Hkv + h / c.G);
+    if (a < 0) return;   // cache reused: the row is left untouched
+    const int32_t* base = c.plan + 4 + P;
+    x0 = ld_const(base, a);
+    ns = ld_const(base, a + 1) - x0;
+    hl = (int64_t)c.G * c.Lb;
+    rem = (int64_t)(h % c.G) * c.Lb + pos;
+  } else {
+    for (int bb = 0; bb < b; ++bb) x0 += splits_of(c.offsets, bb, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
+    ns = splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
+  }
   if (x0 > c.total_splits) x0 = c.total_splits;
   if (ns > c.total_splits - x0) ns = c.total_splits - x0;
   const float le = c.extra_lse ? c.extra_lse[row] : kNegInf;
@@ -1595,6 +1639,105 @@ __global__ void __launch_bounds__(256) chunk_check_kernel(const int32_t* list, c
 }
 
 // ---------------------------------------------------------------------------
+// unit plan of a masked step: one 1024-thread workgroup
+// ---------------------------------------------------------------------------
+//
+// Lists the (stream, KV head) pairs the mask recomputes, in mask order, and
+// sizes their splits so that just those pairs fill the workgroups the
+// all-heads plan would use (cap): the smallest split length (>= min_split
+// tiles) whose workgroups fit, or one split per pair.  A step that recomputes
+// 2 of 12 heads then runs in about 2/12 of a full pass instead of leaving 10/12
+// of the workgroups idle.  Layout: see plan_ints in fb_internal.h.
+
+__device__ __forceinline__ int64_t wg_sum64(int64_t v, int64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();   // red free from any earlier use
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int64_t t = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+__global__ void __launch_bounds__(1024) unit_plan_kernel(const UnitPlanArgs u) {
+  __shared__ int wsum[16];
+  __shared__ int64_t red[16];
+  const int P = u.B * u.Hkv;
+  int32_t* act = u.plan + 4;
+  int32_t* base = act + P;
+  int32_t* slot = base + P + 1;
+  const int tid = threadIdx.x;
+  // the listed pairs, in mask order
+  int n = 0;
+  for (int c0 = 0; c0 < P; c0 += 1024) {
+    const int i = c0 + tid;
+    const int on = i < P && u.mask[i] != 0;
+    const int pos = wg_exclusive_scan(on, wsum);
+    if (i < P) slot[i] = on ? n + pos : -1;
+    if (on) act[n + pos] = i;
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += wsum[w];
+    n += total;
+  }
+  __syncthreads();   // every listed pair written before any thread reads act[]
+  // split length: total tiles of the listed pairs over the cap, raised until
+  // their splits' workgroups fit (or one split per pair)
+  auto tiles_of = [&](int a) -> int64_t {
+    const int b = act[a] / u.Hkv;
+    return (prefix_len(u.offsets, b) + kTile - 1) / kTile;
+  };
+  int64_t tot = 0, mx = 0;
+  for (int a = tid; a < n; a += 1024) {
+    const int64_t t = tiles_of(a);
+    tot += t;
+    mx = t > mx ? t : mx;
+  }
+  tot = wg_sum64(tot, red);
+  // max via the same reduction on a one-hot count per candidate is not
+  // needed: the loop below stops at the longest pair's tile count
+  int64_t mx_all = mx;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int64_t other = __shfl_xor(mx_all, o, 64);
+    mx_all = other > mx_all ? other : mx_all;
+  }
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = mx_all;
+  __syncthreads();
+  mx_all = 0;
+  for (int w = 0; w < 16; ++w) mx_all = red[w] > mx_all ? red[w] : mx_all;
+  int64_t st = ((tot * u.row_tiles) + u.cap - 1) / (u.cap > 0 ? u.cap : 1);
+  if (st < u.min_split) st = u.min_split;
+  for (;;) {
+    int64_t units = 0;
+    for (int a = tid; a < n; a += 1024) units += (tiles_of(a) + st - 1) / st;
+    units = wg_sum64(units, red);
+    if (units * u.row_tiles <= u.cap || st >= mx_all) break;   // uniform over the workgroup
+    ++st;
+  }
+  // first unit of each listed pair
+  int done = 0;
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int a = c0 + tid;
+    const int ns = a < n ? (int)((tiles_of(a) + st - 1) / st) : 0;
+    const int pos = wg_exclusive_scan(ns, wsum);
+    if (a < n) base[a] = done + pos;
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += wsum[w];
+    done += total;
+  }
+  if (tid == 0) {
+    base[n] = done;
+    u.plan[0] = done * u.row_tiles;
+    u.plan[1] = (int)st;
+    u.plan[2] = n;
+    u.plan[3] = done;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // scratch of the no-allocation step (fb_step_noalloc)
 // ---------------------------------------------------------------------------
 //
@@ -1743,6 +1886,11 @@ int launch_chunk_check(const int32_t* list, const int64_t* offsets, int32_t B, i
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
   hipLaunchKernelGGL(chunk_check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, list, offsets, B, Hkv, k,
                      chunk_len, flag);
+  return (int)hipGetLastError();
+}
+
+int launch_unit_plan(const UnitPlanArgs& u, void* stream) {
+  hipLaunchKernelGGL(unit_plan_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, u);
   return (int)hipGetLastError();
 }
 

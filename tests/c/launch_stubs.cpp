@@ -119,6 +119,15 @@ int launch_chunk_check(const int32_t* list, const int64_t* offsets, int32_t B, i
   return 0;
 }
 
+int launch_unit_plan(const UnitPlanArgs& u, void* stream) {
+  (void)stream;
+  ++g_launches;
+  require(u.mask != nullptr && u.plan != nullptr && u.row_tiles >= 1 && u.min_split >= 1 && u.cap >= 0,
+          "unit plan arguments");
+  require((int64_t)u.B * u.Hkv <= ((int64_t)1 << 21), "unit plan pairs");
+  return 0;
+}
+
 int noalloc_scratch(void** ptr) {
   *ptr = (void*)(uintptr_t)0x40000000;   // an aligned stand-in address, never dereferenced on the host
   return 0;

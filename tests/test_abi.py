@@ -55,7 +55,8 @@ def test_workspace_size_matches_split_plan():
     # 128K prefix, 8 KV heads, 256 rows per KV head -> 32 splits of 64 tiles
     d = _desc()
     splits = 32
-    expect = splits * 32 * 64 * 128 * 4 + splits * 32 * 64 * 4
+    plan = 256   # a masked step's unit plan after the partials: 5 + 3 * 8 int32, 256-byte aligned
+    expect = splits * 32 * 64 * 128 * 4 + splits * 32 * 64 * 4 + plan
     assert fbl.fb_workspace_size(d) == expect
     assert fbl.fb_workspace_size(_desc(prefix_offsets_host=[0, 0])) == 256   # empty prefix
     with pytest.raises(fbl.FlashBlockError):
