@@ -11,45 +11,33 @@ enum ChunkMode : int32_t { CHUNKS_ALL = 0, CHUNKS_SELECTED = 1, CHUNKS_COMPLEMEN
 constexpr int kTile = 64;  // keys per LDS tile
 constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
 
-// bf16 kernel configurations.  X(id, rows per wave / 16, waves, LDS stages,
+// bf16 kernel configurations (every one keeps its LDS ring within 64 KB at
+// head_dim 128: rings that placed direct-to-LDS loads at 64 KB and above
+// faulted on MI355X).  X(id, rows per wave / 16, waves, LDS stages,
 // resident workgroups per CU, pass: 1 = split partial of the prefix pass,
 // 0 = block pass with merge, row waves: the first this many waves hold query
 // rows, the others only issue their share of the tile loads).  Query rows
 // per workgroup = row waves * 16 * (rows per wave / 16).
 #define FB_BF16_CFGS(X)                                                \
-  X(0, 1, 2, 4, 1, 1, 2)      /* prefix  32 rows: 2 waves x 16            */ \
-  X(1, 1, 4, 4, 1, 1, 4)      /* prefix  64 rows: 4 waves x 16            */ \
-  X(2, 2, 4, 4, 1, 1, 4)      /* prefix 128 rows: 4 waves x 32            */ \
-  X(3, 2, 8, 4, 1, 1, 8)      /* prefix 256 rows: 8 waves x 32            */ \
   X(4, 1, 4, 2, 2, 0, 4)      /* block   64 rows                          */ \
   X(5, 1, 8, 2, 1, 0, 8)      /* block  128 rows                          */ \
   X(7, 2, 4, 2, 2, 1, 4)      /* prefix 128 rows, 2 workgroups per CU     */ \
-  X(8, 4, 4, 4, 1, 1, 4)      /* prefix 256 rows: 4 waves x 64            */ \
   X(9, 1, 2, 2, 2, 1, 2)      /* prefix  32 rows, 2 workgroups per CU     */ \
   X(10, 1, 4, 2, 2, 1, 4)     /* prefix  64 rows, 2 workgroups per CU     */ \
-  X(12, 1, 8, 4, 1, 1, 8)     /* prefix 128 rows: 8 waves x 16            */ \
   X(18, 2, 8, 2, 1, 0, 8)     /* block  256 rows: 8 waves x 32            */ \
   X(19, 2, 4, 2, 2, 0, 4)     /* block  128 rows, 2 workgroups per CU     */ \
-  X(20, 4, 4, 4, 1, 0, 4)     /* block  256 rows: 4 waves x 64            */ \
   X(21, 1, 2, 2, 2, 0, 2)     /* block   32 rows: 2 waves x 16            */ \
   X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */ \
   X(26, 1, 4, 2, 2, 0, 1)     /* block   16 rows + 3 loading waves        */
 
 enum KernelCfg : int32_t {
-  CFG_P32 = 0,
-  CFG_P64 = 1,
-  CFG_P128 = 2,
-  CFG_P256 = 3,
   CFG_B64 = 4,
   CFG_B128 = 5,
   CFG_P128_X2 = 7,
-  CFG_P256_Q4 = 8,
   CFG_P32_X2 = 9,
   CFG_P64_X2 = 10,
-  CFG_P128_W8 = 12,
   CFG_B256 = 18,
   CFG_B128_X2 = 19,
-  CFG_B256_Q4 = 20,
   CFG_B32 = 21,
   CFG_B32_LD = 22,
   CFG_B16_LD = 26,

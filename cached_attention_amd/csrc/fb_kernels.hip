@@ -377,6 +377,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int NG = 2 * DT;                  // MFMA groups of the PV product
   static_assert(IPT % IPW == 0 && IPW % 2 == 0, "each wave loads an even run of one tensor");
   static_assert(NS >= 2 && NS <= 4, "2..4 stages");
+  // The direct-to-LDS loads address LDS through M0.  Rings reaching 64 KB and
+  // above (3 and 4 stages at head_dim 128) faulted the GPU, so the ring, and
+  // every load destination, stays below 64 KB.
+  static_assert(NS * STAGE <= 65536, "LDS ring within 64 KB");
   static_assert((DIST - 1) * IPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
