@@ -238,6 +238,9 @@ def main() -> int:
                     "its query similarity exceeds gamma")
     ap.add_argument("--prefix-len", type=int, default=0,
                     help="override the workload's prefix length (tokens per stream), e.g. a 128K -> 800K sweep")
+    ap.add_argument("--graph", action="store_true",
+                    help="time whole bench steps as replays of captured HIP graphs (one per KV-cache copy), so "
+                         "the host's launch overhead stays out; per-step latencies stay eager")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip the amd-smi power and clock snapshots (and the extra full-recompute steps "
@@ -373,9 +376,10 @@ def main() -> int:
 
     counter = [0]
 
-    def bench_step(mode, rr):
-        layer = counter[0] % N_LAYERS
-        counter[0] += 1
+    def bench_step(mode, rr, layer=None):
+        if layer is None:
+            layer = counter[0] % N_LAYERS
+            counter[0] += 1
         for j, st in enumerate(states):
             kp, vp = layers[j][layer]
             for s in range(w.steps):
@@ -419,14 +423,37 @@ def main() -> int:
         del g
         return ms
 
+    def graph_steps(mode, rr):
+        """One captured graph per KV-cache copy of a whole bench step; replays
+        rotate over them like the eager steps.  Every launch of the library is a
+        kernel (no memset, no allocation, no host synchronisation)."""
+        graphs = []
+        for layer in range(N_LAYERS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                bench_step(mode, rr, layer)
+            graphs.append(g)
+        turn = [0]
+
+        def replay():
+            graphs[turn[0] % N_LAYERS].replay()
+            turn[0] += 1
+        return replay
+
     gpu_idle = None if args.no_gpu_state else smi_snapshot()
     # ---- whole bench steps: cached (r) and full recompute ----
     for _ in range(args.warmup):
         bench_step("cached", r)
-    ms_cached = timed(lambda: bench_step("cached", r), args.steps)
+    cached_step = graph_steps("cached", r) if args.graph else (lambda: bench_step("cached", r))
+    for _ in range(2 if args.graph else 0):
+        cached_step()
+    ms_cached = timed(cached_step, args.steps)
     for _ in range(max(1, args.warmup // 2)):
         bench_step("full", 1)
-    ms_full = timed(lambda: bench_step("full", 1), args.steps)
+    full_step = graph_steps("full", 1) if args.graph else (lambda: bench_step("full", 1))
+    for _ in range(2 if args.graph else 0):
+        full_step()
+    ms_full = timed(full_step, args.steps)
     q_tokens = w.batch * w.block_len * w.steps * len(blocks)
     gpu_load = (None if args.no_gpu_state
                 else snapshot_under_load(lambda: bench_step("full", 1), torch.cuda.synchronize))
@@ -501,6 +528,32 @@ def main() -> int:
         ms_select = timed(select_rot, n_k)
         ms_select_full = timed(lambda: fbl.fb_select_chunks(st0.desc, q0, layers[0][0][0], 64, k_sel, st0.chunks,
                                                             sel_ws, sel_ws.numel()), n_k)
+    # one refresh step (s = 0) and one reuse step (s = 1) of the first stream
+    # set, each replayed from a graph: device time without host launch gaps.
+    # A gamma step rewrites its reference queries, so a replayed step 1 would
+    # not repeat itself; it is not timed this way.
+    step_graph = None
+    if args.policy != "gamma":
+        kp1, vp1 = layers[0][0]
+
+        def one_step(s):
+            q, k, v = steps_dev[0][s]
+            if args.policy == "fixed":
+                st0.step(q, k, v, kp1, vp1, s, r, "cached", want_lse=False)
+            else:
+                _, kprev, vprev = steps_dev[0][max(s - 1, 0)]
+                st0.step_policy(q, k, v, kprev, vprev, kp1, vp1, s, args.policy, args.tau, args.eps, args.gamma,
+                                want_lse=False)
+
+        if w.steps > 1 and r > 1:
+            step_graph = {"refresh_step": timed_graph(lambda: one_step(0), n_k) * 1e3}
+            if topk:
+                select(0, steps_dev[0][0][0], 0)
+            one_step(0)
+            step_graph["reuse_step"] = timed_graph(lambda: one_step(1), n_k) * 1e3
+            if args.policy != "fixed":
+                torch.cuda.synchronize()
+                step_graph["reuse_step_recompute_fraction"] = float(st0.mask.float().mean())
     tiny = torch.zeros(8, 128, device="cuda")
     tiny_l = torch.zeros(8, device="cuda")
     ms_floor = timed(lambda: fbl.fb_merge(4, 128, tiny, tiny_l, tiny, tiny_l, tiny, tiny_l), 200)
@@ -601,6 +654,7 @@ def main() -> int:
                                       "chunk keys kept per layer, the block's new chunks pooled in the step" if topk
                                       else "seeded random stand-in (fixed)")} if args.sparse else None),
             "step": "one block of denoise_steps attention steps, one layer",
+            "launch": "graph replay" if args.graph else "eager",
             "policy": ({"name": "fixed", "refresh_period": r} if args.policy == "fixed" else
                        {"name": args.policy, "tau": args.tau, "eps": args.eps} if args.policy == "tau" else
                        {"name": "gamma", "gamma": args.gamma}),
@@ -613,6 +667,7 @@ def main() -> int:
                             "reuse_p10": pct(lat["reuse"], 10), "reuse_p90": pct(lat["reuse"], 90),
                             "samples": {"refresh": len(lat["refresh"]), "reuse": len(lat["reuse"])},
                             "launch_floor": ms_floor * 1e3},
+        "step_graph_us": step_graph,
         "block_pass": {"us": ms_block * 1e3, "timing": "graph of back-to-back launches, replayed",
                        "algorithmic_bytes": bb, "algorithmic_flops": bf,
                        "gbs": bb / (ms_block * 1e-3) / 1e9, "tflops": bf / (ms_block * 1e-3) / 1e12,

@@ -680,6 +680,8 @@ fb_status fb_refresh_mask_tau(const fb_desc* d, const void* k_prev, const void* 
   if (!count_out || !mask_out) return fail(FB_ERR_NULL, "count_out and mask_out are required");
   if (step > 0 && (!k_prev || !v_prev || !k_cur || !v_cur))
     return fail(FB_ERR_NULL, "k_prev, v_prev, k_cur and v_cur are required after step 0");
+  if (step > 0 && (!aligned16(k_prev) || !aligned16(v_prev) || !aligned16(k_cur) || !aligned16(v_cur)))
+    return fail(FB_ERR_ALIGN, "k_prev, v_prev, k_cur and v_cur must be 16-byte aligned");
   const size_t need = (size_t)d->batch * d->block_len * sizeof(int32_t);
   if (ws_bytes < need) return fail(FB_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!ws) return fail(FB_ERR_NULL, "workspace is NULL");

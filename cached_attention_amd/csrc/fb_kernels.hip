@@ -1098,37 +1098,71 @@ __device__ __forceinline__ void merge_row(int64_t row, int D, const float* oa, c
 // block-external partial at this step.  They stay on the device: the prefix
 // pass and the split combine read them, so no host round trip decides a step.
 
-__device__ __forceinline__ float ld_elem(const void* p, int64_t i, int dtype) {
-  return dtype == kDtypeBf16 ? (float)((const __bf16*)p)[i] : ((const float*)p)[i];
-}
-
 // threshold-based reuse, part 1: one wave per block token -- did its K or V
 // row (any KV head, any dim) change by more than eps since the previous step?
+// Lanes take 16-byte vectors of the token's Hkv*D elements (8 bf16 or 4 fp32;
+// base pointers and strides are 16-byte aligned), four vectors of each of the
+// four tensors loaded before any is compared, so a token of 8 heads x 128 dims
+// costs one memory round trip rather than one per element group.
+template <typename T>
 __device__ __forceinline__ void tau_flag_token(const TauArgs& t, int64_t tok, int lane);
 
 // one wave per token; the grid strides over the tokens (capped grid)
+template <typename T>
 __global__ void __launch_bounds__(256) tau_flags_kernel(const TauArgs t) {
   const int lane = threadIdx.x & 63;
   const int64_t toks = (int64_t)t.B * t.Lb;
   for (int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tok < toks; tok += (int64_t)gridDim.x * 4)
-    tau_flag_token(t, tok, lane);
+    tau_flag_token<T>(t, tok, lane);
 }
 
+template <typename T>
 __device__ __forceinline__ void tau_flag_token(const TauArgs& t, int64_t tok, int lane) {
   if (t.step == 0) {   // no previous step: every token is new
     if (lane == 0) t.flags[tok] = 1;
     return;
   }
+  typedef f32x4 Raw;                      // 16 bytes of T
+  constexpr int VE = 16 / (int)sizeof(T);  // elements per vector
+  constexpr int U = 4;                     // vectors per lane per round
   const int b = (int)(tok / t.Lb);
   const int pos = (int)(tok % t.Lb);
   const int64_t base = (int64_t)b * t.kv_sb + (int64_t)pos * t.kv_st;
-  const int per = t.Hkv * t.D;
+  const int per_head = t.D / VE;
+  const int nvec = t.Hkv * per_head;
+  const T* kc = (const T*)t.k_cur + base;
+  const T* kp = (const T*)t.k_prev + base;
+  const T* vc = (const T*)t.v_cur + base;
+  const T* vp = (const T*)t.v_prev + base;
   bool changed = false;
-  for (int e = lane; e < per; e += 64) {
-    const int64_t i = base + (int64_t)(e / t.D) * t.kv_sh + e % t.D;
-    const float dk = fabsf(ld_elem(t.k_cur, i, t.dtype) - ld_elem(t.k_prev, i, t.dtype));
-    const float dv = fabsf(ld_elem(t.v_cur, i, t.dtype) - ld_elem(t.v_prev, i, t.dtype));
-    changed |= dk > t.eps || dv > t.eps;
+  for (int e0 = lane; e0 < nvec; e0 += 64 * U) {
+    Raw a[U], p[U], c[U], q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * 64;
+      if (e < nvec) {
+        const int64_t i = (int64_t)(e / per_head) * t.kv_sh + (e % per_head) * VE;
+        a[u] = *(const Raw*)(kc + i);
+        p[u] = *(const Raw*)(kp + i);
+        c[u] = *(const Raw*)(vc + i);
+        q[u] = *(const Raw*)(vp + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (e0 + u * 64 < nvec) {
+        const T* ka = (const T*)&a[u];
+        const T* kb = (const T*)&p[u];
+        const T* va = (const T*)&c[u];
+        const T* vb = (const T*)&q[u];
+#pragma unroll
+        for (int j = 0; j < VE; ++j) {
+          const float dk = fabsf((float)ka[j] - (float)kb[j]);
+          const float dv = fabsf((float)va[j] - (float)vb[j]);
+          changed |= dk > t.eps || dv > t.eps;
+        }
+      }
+    }
   }
   changed = __any(changed);
   if (lane == 0) t.flags[tok] = changed ? 1 : 0;
@@ -1512,7 +1546,7 @@ __device__ __forceinline__ uint32_t rank_key(float s) {
   return ~((u & 0x80000000u) ? ~u : (u | 0x80000000u));
 }
 
-// exclusive prefix sum of v over the 1024 threads of the workgroup
+// exclusive prefix sum of v over the threads of the workgroup (at most 1024)
 __device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -1643,7 +1677,7 @@ __global__ void __launch_bounds__(256) chunk_check_kernel(const int32_t* list, c
 }
 
 // ---------------------------------------------------------------------------
-// unit plan of a masked step: one 1024-thread workgroup
+// unit plan of a masked step: one 256-thread workgroup
 // ---------------------------------------------------------------------------
 //
 // Lists the (stream, KV head) pairs the mask recomputes, in mask order, and
@@ -1652,85 +1686,119 @@ __global__ void __launch_bounds__(256) chunk_check_kernel(const int32_t* list, c
 // tiles) whose workgroups fit, or one split per pair.  A step that recomputes
 // 2 of 12 heads then runs in about 2/12 of a full pass instead of leaving 10/12
 // of the workgroups idle.  Layout: see plan_ints in fb_internal.h.
+//
+// Thread t takes pairs t, t + 256, ...; the first of them stays in registers
+// between the phases (all of them when B * Hkv <= 256), the others are read
+// again.  The mask and the stream's tile count are loaded together, so a step
+// with few pairs costs two dependent memory round trips and a handful of
+// barriers.
 
-__device__ __forceinline__ int64_t wg_sum64(int64_t v, int64_t* red) {
+constexpr int kPlanThreads = 256;
+
+// sum and max over the workgroup in one exchange; red holds 2 * waves values
+__device__ __forceinline__ void wg_sum_max64(int64_t& s, int64_t& m, int64_t* red) {
+  constexpr int kWaves = kPlanThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 32; o >= 1; o >>= 1) {
+    s += __shfl_xor(s, o, 64);
+    const int64_t other = __shfl_xor(m, o, 64);
+    m = other > m ? other : m;
+  }
   __syncthreads();   // red free from any earlier use
-  if (lane == 0) red[wave] = v;
+  if (lane == 0) {
+    red[wave] = s;
+    red[kWaves + wave] = m;
+  }
   __syncthreads();
-  int64_t t = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  s = 0;
+  m = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    s += red[w];
+    m = red[kWaves + w] > m ? red[kWaves + w] : m;
+  }
+}
+
+__device__ __forceinline__ int wg_total(const int* wsum) {
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / 64; ++w) t += wsum[w];
   return t;
 }
 
-__global__ void __launch_bounds__(1024) unit_plan_kernel(const UnitPlanArgs u) {
-  __shared__ int wsum[16];
-  __shared__ int64_t red[16];
+__global__ void __launch_bounds__(kPlanThreads) unit_plan_kernel(const UnitPlanArgs u) {
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ int64_t red[2 * (kPlanThreads / 64)];
   const int P = u.B * u.Hkv;
   int32_t* act = u.plan + 4;
   int32_t* base = act + P;
   int32_t* slot = base + P + 1;
   const int tid = threadIdx.x;
-  // the listed pairs, in mask order
-  int n = 0;
-  for (int c0 = 0; c0 < P; c0 += 1024) {
+  // this thread's pair in a chunk: recomputed?, and its stream's tile count
+  // (0 if not recomputed); the first chunk's values stay in registers
+  int on0 = 0, slot0 = -1;
+  int64_t t0 = 0;
+  auto pair = [&](int c0, int& on, int64_t& t) {
+    if (c0 == 0) {
+      on = on0;
+      t = t0;
+      return;
+    }
     const int i = c0 + tid;
-    const int on = i < P && u.mask[i] != 0;
-    const int pos = wg_exclusive_scan(on, wsum);
-    if (i < P) slot[i] = on ? n + pos : -1;
-    if (on) act[n + pos] = i;
-    int total = 0;
-    for (int w = 0; w < 16; ++w) total += wsum[w];
-    n += total;
-  }
-  __syncthreads();   // every listed pair written before any thread reads act[]
-  // split length: total tiles of the listed pairs over the cap, raised until
-  // their splits' workgroups fit (or one split per pair)
-  auto tiles_of = [&](int a) -> int64_t {
-    const int b = act[a] / u.Hkv;
-    return (prefix_len(u.offsets, b) + kTile - 1) / kTile;
+    on = i < P && u.mask[i] != 0;
+    t = on ? (prefix_len(u.offsets, i / u.Hkv) + kTile - 1) / kTile : 0;
   };
+  if (tid < P) {   // both loads in flight together
+    const int64_t lp = prefix_len(u.offsets, tid / u.Hkv);
+    on0 = u.mask[tid] != 0;
+    t0 = on0 ? (lp + kTile - 1) / kTile : 0;
+  }
+  // the listed pairs, in mask order; total and longest tile count
+  int n = 0;
   int64_t tot = 0, mx = 0;
-  for (int a = tid; a < n; a += 1024) {
-    const int64_t t = tiles_of(a);
+  for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
+    int on;
+    int64_t t;
+    pair(c0, on, t);
+    const int pos = wg_exclusive_scan(on, wsum);
+    const int i = c0 + tid;
+    const int sl = on ? n + pos : -1;
+    if (i < P) slot[i] = sl;
+    if (c0 == 0) slot0 = sl;
+    if (on) act[n + pos] = i;
+    n += wg_total(wsum);
     tot += t;
     mx = t > mx ? t : mx;
   }
-  tot = wg_sum64(tot, red);
-  // max via the same reduction on a one-hot count per candidate is not
-  // needed: the loop below stops at the longest pair's tile count
-  int64_t mx_all = mx;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const int64_t other = __shfl_xor(mx_all, o, 64);
-    mx_all = other > mx_all ? other : mx_all;
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = mx_all;
-  __syncthreads();
-  mx_all = 0;
-  for (int w = 0; w < 16; ++w) mx_all = red[w] > mx_all ? red[w] : mx_all;
+  wg_sum_max64(tot, mx, red);
+  // split length: total tiles of the listed pairs over the cap, raised until
+  // their splits' workgroups fit (or one split per pair)
   int64_t st = ((tot * u.row_tiles) + u.cap - 1) / (u.cap > 0 ? u.cap : 1);
   if (st < u.min_split) st = u.min_split;
   for (;;) {
-    int64_t units = 0;
-    for (int a = tid; a < n; a += 1024) units += (tiles_of(a) + st - 1) / st;
-    units = wg_sum64(units, red);
-    if (units * u.row_tiles <= u.cap || st >= mx_all) break;   // uniform over the workgroup
+    int64_t units = 0, unused = 0;
+    for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
+      int on;
+      int64_t t;
+      pair(c0, on, t);
+      units += (t + st - 1) / st;   // 0 for a pair that is not recomputed
+    }
+    wg_sum_max64(units, unused, red);
+    if (units * u.row_tiles <= u.cap || st >= mx) break;   // uniform over the workgroup
     ++st;
   }
-  // first unit of each listed pair
+  // first unit of each listed pair (the scan runs in mask order, which is the
+  // listed order)
   int done = 0;
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int a = c0 + tid;
-    const int ns = a < n ? (int)((tiles_of(a) + st - 1) / st) : 0;
+  for (int c0 = 0; c0 < P; c0 += kPlanThreads) {
+    int on;
+    int64_t t;
+    pair(c0, on, t);
+    const int ns = on ? (int)((t + st - 1) / st) : 0;
     const int pos = wg_exclusive_scan(ns, wsum);
-    if (a < n) base[a] = done + pos;
-    int total = 0;
-    for (int w = 0; w < 16; ++w) total += wsum[w];
-    done += total;
+    if (on) base[c0 == 0 ? slot0 : slot[c0 + tid]] = done + pos;
+    done += wg_total(wsum);
   }
   if (tid == 0) {
     base[n] = done;
@@ -1841,7 +1909,10 @@ int launch_merge(int64_t rows, int32_t head_dim, const float* oa, const float* l
 int launch_tau(const TauArgs& t, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const int64_t toks = (int64_t)t.B * t.Lb;
-  hipLaunchKernelGGL(tau_flags_kernel, capped_grid((toks + 3) / 4), dim3(256), 0, s, t);
+  if (t.dtype == kDtypeBf16)
+    hipLaunchKernelGGL(tau_flags_kernel<__bf16>, capped_grid((toks + 3) / 4), dim3(256), 0, s, t);
+  else
+    hipLaunchKernelGGL(tau_flags_kernel<float>, capped_grid((toks + 3) / 4), dim3(256), 0, s, t);
   hipLaunchKernelGGL(tau_finalize_kernel, dim3((unsigned)t.B), dim3(256), 0, s, t);
   return (int)hipGetLastError();
 }
@@ -1894,7 +1965,7 @@ int launch_chunk_check(const int32_t* list, const int64_t* offsets, int32_t B, i
 }
 
 int launch_unit_plan(const UnitPlanArgs& u, void* stream) {
-  hipLaunchKernelGGL(unit_plan_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, u);
+  hipLaunchKernelGGL(unit_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, u);
   return (int)hipGetLastError();
 }
 

@@ -222,7 +222,8 @@ fb_status fb_step_noalloc(const fb_desc* d, const void* q_blk, const void* k_blk
  * previous step's by more than eps (max-abs); every KV head of the stream is
  * recomputed iff M >= tau (the cache is reused while M < tau).  k_prev/v_prev
  * are the previous step's block K/V in the fb_desc block layout (not read at
- * step 0).  Writes count_out [B] (M; Lb at step 0) and mask_out [B][Hkv].  ws
+ * step 0); after step 0 all four base pointers must be 16-byte aligned
+ * (FB_ERR_ALIGN otherwise).  Writes count_out [B] (M; Lb at step 0) and mask_out [B][Hkv].  ws
  * holds B*Lb int32 flags (fb_workspace_size covers it).
  *
  * fb_refresh_mask_gamma: head-wise selection.  For each query head, the cosine

@@ -131,13 +131,14 @@ def test_adaptive_reuse_validation():
     lib = fbl.lib()
     ws_b = fbl.fb_workspace_size(d)
     tau = lambda **kw: lib.fb_refresh_mask_tau(
-        kw.get("d", d.ref), FAKE, FAKE, FAKE, FAKE, kw.get("eps", 0.1), 3, kw.get("step", 1),
+        kw.get("d", d.ref), FAKE, FAKE, kw.get("kc", FAKE), FAKE, kw.get("eps", 0.1), 3, kw.get("step", 1),
         kw.get("cnt", FAKE), kw.get("mask", FAKE), kw.get("ws", FAKE), kw.get("wsb", ws_b), None)
     assert tau(d=None) == fbl.FB_ERR_NULL
     assert tau(step=-1) == fbl.FB_ERR_ARG
     assert tau(eps=-1.0) == fbl.FB_ERR_ARG
     assert tau(eps=float("nan")) == fbl.FB_ERR_ARG
     assert tau(mask=None) == fbl.FB_ERR_NULL
+    assert tau(kc=FAKE + 8) == fbl.FB_ERR_ALIGN   # rows move as 16-byte vectors
     assert tau(wsb=1 * 64 * 4 - 1) == fbl.FB_ERR_WORKSPACE   # B * Lb int32 flags
     assert ws_b >= 1 * 64 * 4
     gam = lambda **kw: lib.fb_refresh_mask_gamma(kw.get("d", d.ref), FAKE, kw.get("qr", FAKE),
