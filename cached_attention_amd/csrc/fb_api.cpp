@@ -61,9 +61,12 @@ int prefix_cfg(const fb_desc* d) {
   // (their waves drift apart, so one's softmax overlaps the other's MFMAs);
   // up to 64 rows four 16-row waves, also for 32 rows, where the upper two
   // only issue tile loads: every wave then issues half the loads, and the
-  // pass runs 5-8% faster than with two waves; 256-row KV heads take two
-  // 128-row tiles that share K/V through L2
-  return rows <= 64 ? fb::CFG_P64_X2 : fb::CFG_P128_X2;
+  // pass runs 5-8% faster than with two waves.  A KV head of 129..256 rows
+  // takes one 8-wave workgroup, which fetches each tile once: at the board's
+  // power cap, where a long pass settles, the halved HBM and DMA traffic buys
+  // a higher clock (5% faster than two 128-row workgroups sharing K/V through
+  // L2).  Larger blocks take 128-row tiles (less padding in the last tile).
+  return rows <= 64 ? fb::CFG_P64_X2 : rows <= 128 ? fb::CFG_P128_X2 : rows <= 256 ? fb::CFG_P256 : fb::CFG_P128_X2;
 #endif
 }
 int block_cfg(const fb_desc* d) {

@@ -28,7 +28,8 @@ constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
   X(19, 2, 4, 2, 2, 0, 4)     /* block  128 rows, 2 workgroups per CU     */ \
   X(21, 1, 2, 2, 2, 0, 2)     /* block   32 rows: 2 waves x 16            */ \
   X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */ \
-  X(26, 1, 4, 2, 2, 0, 1)     /* block   16 rows + 3 loading waves        */
+  X(26, 1, 4, 2, 2, 0, 1)     /* block   16 rows + 3 loading waves        */ \
+  X(27, 2, 8, 2, 1, 1, 8)     /* prefix 256 rows: 8 waves x 32            */
 
 enum KernelCfg : int32_t {
   CFG_B64 = 4,
@@ -41,6 +42,7 @@ enum KernelCfg : int32_t {
   CFG_B32 = 21,
   CFG_B32_LD = 22,
   CFG_B16_LD = 26,
+  CFG_P256 = 27,
 };
 
 struct CfgInfo {
