@@ -99,7 +99,18 @@ struct TileIter {
   int nlist, ptr, mode, ct;
 };
 
+// DENSE: the caller knows the iterator walks every position (no chunk list),
+// so the chunk-mode code is left out of its tile loop
+template <bool DENSE = false>
 __device__ __forceinline__ bool next_tile(TileIter& it, int64_t& tok0, int& nvalid) {
+  if (DENSE || it.mode == CHUNKS_ALL) {   // wave-uniform: one scalar branch per tile
+    if (it.lt >= it.lt_end) return false;
+    const int64_t start = (int64_t)(it.lt++) * kTile;
+    tok0 = start;
+    const int64_t rem = it.lp - start;
+    nvalid = rem < kTile ? (int)rem : kTile;
+    return true;
+  }
   while (it.lt < it.lt_end) {
     const int i = it.lt++;
     int64_t start;
@@ -340,8 +351,19 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void* s
 #ifndef FB_K_AHEAD
 #define FB_K_AHEAD 1
 #endif
-constexpr int kVAhead = FB_V_AHEAD;   // V^T fragment groups read ahead of their MFMAs
-constexpr int kKAhead = FB_K_AHEAD;   // K fragment k-steps read ahead of their MFMAs
+#ifndef FB_V_AHEAD_Q1
+#define FB_V_AHEAD_Q1 FB_V_AHEAD
+#endif
+#ifndef FB_K_AHEAD_Q1
+#define FB_K_AHEAD_Q1 FB_K_AHEAD
+#endif
+// V^T fragment groups / K fragment k-steps read ahead of their MFMAs, for
+// 32-row waves (QT = 2) and for 16-row waves (QT = 1), whose MFMA groups are
+// half as long and cover less of the LDS latency
+template <int QT>
+constexpr int v_ahead() { return QT == 1 ? FB_V_AHEAD_Q1 : FB_V_AHEAD; }
+template <int QT>
+constexpr int k_ahead() { return QT == 1 ? FB_K_AHEAD_Q1 : FB_K_AHEAD; }
 #ifndef FB_PV_DEFER
 #define FB_PV_DEFER 2
 #endif
@@ -368,6 +390,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int CH = D / 8;                   // 16-byte slots per key row
   constexpr int ROWS = RW * 16 * QT;          // query rows per workgroup (waves 0 .. RW-1)
   static_assert(RW >= 1 && RW <= NW, "row waves");
+  constexpr int kVAhead = v_ahead<QT>();
+  constexpr int kKAhead = k_ahead<QT>();
   constexpr int TBYTES = kTile * D * 2;       // one K or V tile
   constexpr int STAGE = 2 * TBYTES;
   constexpr int IPT = TBYTES / 1024;          // 1 KB direct-to-LDS loads per tile and tensor
@@ -479,16 +503,17 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   auto issue = [&](int stage, int64_t tok0, int nvalid) __attribute__((always_inline)) {
     const char* g = gsrc + tok0 * row_bytes;
     const uint32_t dst = lds_dst + stage * STAGE;
+    if (nvalid < kTile) {   // ragged tile: rows past the end re-read the last key (masked later)
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int jj = jj0 + u;
-      if (nvalid < kTile) {   // ragged tile: rows past the end re-read the last key (masked later)
-        const int row = jj * RPI + lane / CH;
+      for (int u = 0; u < IPW; ++u) {
+        const int row = (jj0 + u) * RPI + lane / CH;
         const int srow = row < nvalid ? row : nvalid - 1;
         dma16(dst + u * 1024, (uint32_t)(srow * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16, g);
-      } else {
-        dma16(dst + u * 1024, lane_part[u & 1] + (uint32_t)((jj - (u & 1)) * RPI * row_bytes), g);
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < IPW; ++u)
+        dma16(dst + u * 1024, lane_part[u & 1] + (uint32_t)((jj0 + u - (u & 1)) * RPI * row_bytes), g);
     }
   };
 
@@ -675,7 +700,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // one tile: wait for it (tiles issued after it may stay in flight), one
   // barrier (every wave is done with the stage refilled next), issue the tile
   // DIST ahead, compute, advance the queue
-  auto tile_step = [&](auto mode_tag, auto pend_tag) __attribute__((always_inline)) {
+  auto tile_step = [&](auto mode_tag, auto pend_tag, auto dense_tag) __attribute__((always_inline)) {
+    constexpr bool kDense = decltype(dense_tag)::value != 0 || !PARTIAL;
     int after = 0;
 #pragma unroll
     for (int j = 1; j < DIST; ++j) after += q_have[j] ? 1 : 0;
@@ -683,7 +709,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     lds_dma_barrier();
     const uint32_t kb = lds0 + st * STAGE;
     if (wave_active) scores_begin(kb);   // stage st is read, stage st + DIST filled: independent
-    q_have[DIST] = q_have[DIST - 1] && next_tile(wk.it, q_tok[DIST], q_nv[DIST]);
+    q_have[DIST] = q_have[DIST - 1] && next_tile<kDense>(wk.it, q_tok[DIST], q_nv[DIST]);
     if (q_have[DIST]) issue((st + DIST) % NS, q_tok[DIST], q_nv[DIST]);
     if (wave_active) {
       scores(kb, pend_tag);
@@ -700,26 +726,34 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   };
   // one pass over the tiles of the split (its first tile in mode first_tag,
   // the others in mode rest_tag); false if it has none
-  auto run_pass = [&](auto first_tag, auto rest_tag) __attribute__((always_inline)) -> bool {
+  // dense_tag 1: the split walks every prefix position (no chunk list), so
+  // its tile loop carries no chunk-mode code
+  auto run_pass = [&](auto first_tag, auto rest_tag, auto dense_tag) __attribute__((always_inline)) -> bool {
+    constexpr bool kDense = decltype(dense_tag)::value != 0 || !PARTIAL;
     st = 0;
 #pragma unroll
     for (int j = 0; j < DIST; ++j) {
-      q_have[j] = (j == 0 || q_have[j - 1]) && next_tile(wk.it, q_tok[j], q_nv[j]);
+      q_have[j] = (j == 0 || q_have[j - 1]) && next_tile<kDense>(wk.it, q_tok[j], q_nv[j]);
       if (q_have[j]) issue(j, q_tok[j], q_nv[j]);
     }
     if (!q_have[0]) return false;
     // PV groups deferred by a tile run at the start of the next tile of the
     // same pass, and at the pass's end (scores-only passes defer nothing)
     constexpr bool defer = kPvDefer > 0 && decltype(rest_tag)::value != 2;
-    tile_step(first_tag, IC<0>{});
-    while (q_have[0]) tile_step(rest_tag, IC<defer ? 1 : 0>{});
+    tile_step(first_tag, IC<0>{}, dense_tag);
+    while (q_have[0]) tile_step(rest_tag, IC<defer ? 1 : 0>{}, dense_tag);
     if constexpr (defer) {
       if (wave_active) run_deferred();
     }
     return true;
   };
   const TileIter it0 = wk.it;
-  if (run_pass(IC<1>{}, IC<0>{})) {
+  // the main pass with its tile loop specialised for dense splits (the
+  // prefix pass without a chunk list, and every block pass); the rare
+  // rerun passes below take the general loop
+  const bool ran = (!PARTIAL || wk.it.mode == CHUNKS_ALL) ? run_pass(IC<1>{}, IC<0>{}, IC<1>{})
+                                                        : run_pass(IC<1>{}, IC<0>{}, IC<0>{});
+  if (ran) {
     // did a score outrun its row's reference?  (l bounds every p of the row)
     bool redo = false;
 #pragma unroll
@@ -728,7 +762,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     __syncthreads();
     if (wg_redo) {   // rare: the split's exact row maxima, then the pass again against them
       wk.it = it0;
-      run_pass(IC<2>{}, IC<2>{});
+      run_pass(IC<2>{}, IC<2>{}, IC<0>{});
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         float mx = mx_lane[qt];
@@ -740,7 +774,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
         for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
       wk.it = it0;
-      run_pass(IC<0>{}, IC<0>{});
+      run_pass(IC<0>{}, IC<0>{}, IC<0>{});
     }
   }
 
@@ -850,7 +884,7 @@ __global__ void __launch_bounds__(256) attn_f32m(const AttnArgs a) {
   const int64_t row_bytes = a.kv_st * 4;
   int64_t tok0;
   int nvalid;
-  while (next_tile(wk.it, tok0, nvalid)) {
+  while (next_tile<!PARTIAL>(wk.it, tok0, nvalid)) {
     __syncthreads();   // every wave is done with the previous tile
     for (int idx = tid; idx < kTile * (D / 4); idx += 256) {
       const int t = idx / (D / 4), ch = idx % (D / 4);
