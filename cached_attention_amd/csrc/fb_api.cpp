@@ -61,12 +61,16 @@ int prefix_cfg(const fb_desc* d) {
   // (their waves drift apart, so one's softmax overlaps the other's MFMAs);
   // up to 64 rows four 16-row waves, also for 32 rows, where the upper two
   // only issue tile loads: every wave then issues half the loads, and the
-  // pass runs 5-8% faster than with two waves.  A KV head of 129..256 rows
-  // takes one 8-wave workgroup, which fetches each tile once: at the board's
-  // power cap, where a long pass settles, the halved HBM and DMA traffic buys
-  // a higher clock (5% faster than two 128-row workgroups sharing K/V through
-  // L2).  Larger blocks take 128-row tiles (less padding in the last tile).
-  return rows <= 64 ? fb::CFG_P64_X2 : rows <= 128 ? fb::CFG_P128_X2 : rows <= 256 ? fb::CFG_P256 : fb::CFG_P128_X2;
+  // pass runs 5-8% faster than with two waves.  Above 128 rows, 256-row
+  // tiles of one 8-wave workgroup each fetch every KV tile once per 256 rows:
+  // 5% faster at 256 rows (128K GQA, where the board's power cap sets the
+  // clock and the halved HBM and DMA traffic buys clock), 6% on the
+  // 1560-row video prefix (MFMA-bound) despite its longer padded last tile.
+  // They are taken unless they pad more than an eighth beyond 128-row tiles.
+  if (rows <= 64) return fb::CFG_P64_X2;
+  if (rows <= 128) return fb::CFG_P128_X2;
+  const int64_t pad256 = ceil_div(rows, 256) * 256, pad128 = ceil_div(rows, 128) * 128;
+  return pad256 * 8 <= pad128 * 9 ? fb::CFG_P256 : fb::CFG_P128_X2;
 #endif
 }
 int block_cfg(const fb_desc* d) {
