@@ -208,3 +208,28 @@ def test_step_masked_unit_plan(pattern, dtype):
                     assert torch.equal(g.lse_ext[b, hs], before[1][b, hs])
         err = np.abs(g.o.float().cpu().numpy() - ref.out[s]).max()
         assert err <= tol(w, ref.out[s]), f"step {s}: max|O - O_ref| = {err:.3e}"
+
+
+def test_step_masked_many_pairs():
+    """More (stream, KV head) pairs than the unit-plan workgroup has threads
+    (36 streams x 8 KV heads = 288 > 256), so the plan is built over two
+    chunks of pairs: a seeded mixed mask recomputes exactly its pairs, the
+    others' cache rows stay bit for bit, and every output follows the oracle."""
+    w, p, blk = _setup("bf16", 36, 8, 8, 64, 4, 200, 2, 0.05, seed=61)
+    g = Gpu(w, p, blk)
+    rng = np.random.default_rng(62)
+    mixed = (rng.random((w.batch, w.hkv)) < 0.4).astype(np.int32)
+    assert 0 < mixed.sum() < mixed.size and w.batch * w.hkv > 256
+    masks = [np.ones((w.batch, w.hkv), np.int32), mixed]
+    ref = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, 1 / math.sqrt(w.head_dim),
+                                  "given", masks=masks)
+    for s in range(w.steps):
+        before = (g.o_ext.clone(), g.lse_ext.clone())
+        g.mask.copy_(torch.from_numpy(masks[s]))
+        g.step(s)
+        torch.cuda.synchronize()
+        keep = torch.from_numpy(masks[s] == 0).to("cuda")   # [B][Hkv], G = 1
+        assert torch.equal(g.o_ext[keep], before[0][keep]), f"step {s}: a reused cache row moved"
+        assert torch.equal(g.lse_ext[keep], before[1][keep])
+        err = np.abs(g.o.float().cpu().numpy() - ref.out[s]).max()
+        assert err <= tol(w, ref.out[s]), f"step {s}: max|O - O_ref| = {err:.3e}"
