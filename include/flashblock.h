@@ -235,11 +235,13 @@ fb_status fb_step_noalloc(const fb_desc* d, const void* q_blk, const void* k_blk
  * [B][Hq] fp32 and mask_out.  At step 0 q_ref may hold anything.
  *
  * fb_step_masked: one dense step under a mask: the prefix pass and split
- * combine run only for the (stream, KV head) pairs the mask selects (the
- * others' workgroups exit at once and their rows of o_ext_cache / lse_ext_cache
- * stay as they are), then the in-block pass merges with the cache for every
- * head into o.  The mask is read on the device, so no host synchronisation is
- * needed between the mask call and the step. */
+ * combine run only for the (stream, KV head) pairs the mask selects.  A
+ * device-side unit plan (built from the mask in a small kernel, kept in ws)
+ * lists those pairs and sizes their splits so that they alone fill the
+ * grid; the other pairs get no work and their rows of o_ext_cache /
+ * lse_ext_cache stay as they are.  Then the in-block pass merges with the
+ * cache for every head into o.  The mask is read on the device, so no host
+ * synchronisation is needed between the mask call and the step. */
 fb_status fb_refresh_mask_tau(const fb_desc* d, const void* k_prev, const void* v_prev, const void* k_cur,
                               const void* v_cur, float eps, int32_t tau, int32_t step, int32_t* count_out,
                               int32_t* mask_out, void* ws, size_t ws_bytes, void* stream);
