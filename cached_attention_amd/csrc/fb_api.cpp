@@ -538,6 +538,8 @@ fb_status fb_prefix_combine(const fb_desc* d, const fb_sparse* sp, const float* 
   if (!o_ext || !lse_ext) return fail(FB_ERR_NULL, "o_ext and lse_ext are required");
   if ((extra_o == nullptr) != (extra_lse == nullptr))
     return fail(FB_ERR_NULL, "extra_o and extra_lse must be both given or both NULL");
+  if (!aligned16(o_ext) || (extra_o && !aligned16(extra_o)))
+    return fail(FB_ERR_ALIGN, "o_ext and extra_o must be 16-byte aligned");
   st = check_ws(ws, ws_bytes, workspace_for(d, sp));
   if (st != FB_OK) return st;
   return run_combine(d, sp ? sp->mode : fb::CHUNKS_ALL, sp, extra_o, extra_lse, o_ext, lse_ext, ws, ws_bytes,

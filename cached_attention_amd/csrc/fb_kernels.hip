@@ -1171,7 +1171,15 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs c, int64
 
 template <int D>
 __device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, int lane) {
-  constexpr int PER = D / 64;
+  // Each load instruction moves 16 bytes per lane, so one instruction covers
+  // RPL partial rows (lane group q = lane / (D/4) takes split x + q, dims
+  // 4*(lane % (D/4)) .. +3), and four instructions keep 4*RPL partial rows in
+  // flight per wave; past the row's last split the loads are masked off.
+  constexpr int LPR = D / 4;        // lanes per partial row
+  constexpr int RPL = 64 / LPR;     // partial rows per load instruction
+  constexpr int U = 4;              // load instructions in flight
+  const int q = lane / LPR;
+  const int d0 = (lane % LPR) * 4;
   const int64_t hl_out = (int64_t)c.Hq * c.Lb;
   const int b = (int)(row / hl_out);
   // partial rows of this output row: split x of its run is (x0 + x) * hl + rem
@@ -1199,59 +1207,47 @@ __device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, i
   for (int x = lane; x < ns; x += 64) mx = fmaxf(mx, c.part_lse[(int64_t)(x0 + x) * hl + rem]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;   // this lane group's splits
   if (mx != kNegInf) {
     for (int x1 = 0; x1 < ns; x1 += 64) {
       const int nx = min(64, ns - x1);
-      // lane j holds the weight of split x1 + j
+      // lane j holds the weight of split x1 + j (0 past the last split)
       const float wl = lane < nx ? expf(c.part_lse[(int64_t)(x0 + x1 + lane) * hl + rem] - mx) : 0.f;
-      int j = 0;
-      for (; j + 4 <= nx; j += 4) {   // four partial rows in flight
-        float w4[4];
-        f32x4 v4[4];
+      for (int j = 0; j < nx; j += U * RPL) {
+        float w4[U];
+        f32x4 v4[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          w4[u] = __shfl(wl, j + u, 64);
-          const float* po = c.part_o + ((int64_t)(x0 + x1 + j + u) * hl + rem) * D + lane * PER;
-          if constexpr (PER == 2) {
-            const f32x4 t = {po[0], po[1], 0.f, 0.f};
-            v4[u] = t;
-          } else {
-            const f32x4 t = {po[0], 0.f, 0.f, 0.f};
-            v4[u] = t;
-          }
+        for (int u = 0; u < U; ++u) {
+          const int jj = j + u * RPL + q;   // this lane's split within the 64
+          w4[u] = __shfl(wl, jj < 64 ? jj : 63, 64);
+          v4[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          if (jj < nx) v4[u] = *(const f32x4*)(c.part_o + ((int64_t)(x0 + x1 + jj) * hl + rem) * D + d0);
+          else w4[u] = 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
           wsum += w4[u];
-#pragma unroll
-          for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w4[u], v4[u][i], acc[i]);
+          acc = w4[u] * v4[u] + acc;
         }
       }
-      for (; j < nx; ++j) {
-        const float w = __shfl(wl, j, 64);
-        const float* po = c.part_o + ((int64_t)(x0 + x1 + j) * hl + rem) * D + lane * PER;
-        wsum += w;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, po[i], acc[i]);
-      }
     }
-    if (c.extra_lse) {
-      const float w = expf(le - mx);
-      wsum += w;
-      const float* po = c.extra_o + row * D + lane * PER;
+  }
+  // the lane groups' sums, then the extra partial
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, po[i], acc[i]);
-    }
+  for (int m = LPR; m < 64; m <<= 1) {
+    wsum += __shfl_xor(wsum, m, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], m, 64);
+  }
+  if (mx != kNegInf && c.extra_lse) {
+    const float w = expf(le - mx);
+    wsum += w;
+    acc = w * *(const f32x4*)(c.extra_o + row * D + d0) + acc;
   }
   const bool any = wsum > 0.f;
   const float inv = any ? 1.f / wsum : 0.f;
-  float* op = c.o + row * D + lane * PER;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) op[i] = acc[i] * inv;
+  if (q == 0) *(f32x4*)(c.o + row * D + d0) = acc * inv;
   if (lane == 0) c.lse[row] = any ? mx + logf(wsum) : kNegInf;
 }
 

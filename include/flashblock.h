@@ -140,7 +140,9 @@ fb_status fb_prefix_attn(const fb_desc* d, const void* q_blk, const void* k_pre,
  * equation applied across the splits), optionally folding in one more partial
  * (extra_o [B][Hq][Lb][D], extra_lse [B][Hq][Lb], both or neither -- the
  * sparse variant's cached residual), into o_ext / lse_ext.  `sp` must be the
- * same fb_sparse (or NULL) as for the partials call. */
+ * same fb_sparse (or NULL) as for the partials call.  o_ext and extra_o are
+ * read and written as 16-byte vectors: both must be 16-byte aligned
+ * (FB_ERR_ALIGN otherwise). */
 fb_status fb_prefix_partials(const fb_desc* d, const void* q_blk, const void* k_pre,
                              const void* v_pre, const fb_sparse* sp, void* ws,
                              size_t ws_bytes, void* stream);

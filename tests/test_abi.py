@@ -118,6 +118,19 @@ def test_block_attn_and_merge_validation():
     assert lib.fb_merge(0, 128, None, None, None, None, None, None, None) == fbl.FB_OK
 
 
+def test_prefix_combine_validation():
+    """The split combine reads and writes 16-byte vectors: o_ext and the extra
+    partial must be 16-byte aligned; extra_o / extra_lse come together."""
+    d = _desc()
+    lib = fbl.lib()
+    wsb = fbl.fb_workspace_size(d)
+    comb = lambda oe=FAKE, eo=None, el=None: lib.fb_prefix_combine(d.ref, None, eo, el, oe, FAKE, FAKE, wsb, None)
+    assert comb(oe=FAKE + 8) == fbl.FB_ERR_ALIGN
+    assert comb(eo=FAKE + 4, el=FAKE) == fbl.FB_ERR_ALIGN
+    assert comb(eo=FAKE, el=None) == fbl.FB_ERR_NULL
+    assert comb(oe=None) == fbl.FB_ERR_NULL
+
+
 def test_desc_struct_layout():
     # fb_desc: 7 int32 + float, 2 pointers, 8 int64 strides
     assert ctypes.sizeof(fbl.fb_desc) == 32 + 16 + 64
