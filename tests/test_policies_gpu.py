@@ -93,6 +93,26 @@ def test_tau_mask_counts_exact(dtype, d, seed):
     assert seen == {0, 1}   # the threshold both reuses and recomputes in this block
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tau_mask_counts_exact_long_block(dtype):
+    """A 300-token block with head_dim 64, bf16 and fp32 (4 or 8 elements per
+    16-byte vector): per-stream counts and masks compared exactly, with the
+    threshold both reusing and recomputing."""
+    w, p, blk = _setup(dtype, 2, 8, 2, 64, 300, 300, 6, 0.05, seed=41)
+    g = Gpu(w, p, blk)
+    eps, tau = 0.5, 60
+    ref = oracle.run_block_policy(p.k, p.v, p.offsets, blk.q, blk.k, blk.v, 1 / math.sqrt(w.head_dim),
+                                  "tau", tau=tau, eps=eps)
+    seen = set()
+    for s in range(w.steps):
+        g.tau(s, eps, tau)
+        torch.cuda.synchronize()
+        assert g.count.cpu().numpy().tolist() == ref.counts[s].tolist(), f"step {s}"
+        np.testing.assert_array_equal(g.mask.cpu().numpy(), ref.masks[s])
+        seen.add(int(ref.masks[s][0, 0]))
+    assert seen == {0, 1}
+
+
 def _gamma_case(dtype="bf16"):
     w, p, blk = _setup(dtype, 1, 6, 6, 128, 100, 200, 5, 0.1, seed=43, head_spread=0.9, reveal=False)
     gamma = 0.993
