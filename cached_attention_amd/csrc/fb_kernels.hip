@@ -21,17 +21,20 @@
 // pool / score / topk
 //            -- chunk selection for the sparse variant: mean-pooled chunk
 //              keys, max query score per chunk, top-k by radix select.
-// flag_clear / nan_scan
-//            -- the opt-in debug check of a cache before a reuse step.
+// flag_clear / nan_scan / chunk_check
+//            -- the opt-in debug checks (a cache before a reuse step, a
+//              sparse chunk list).
+// unit_plan  -- the device work list of a masked step: the recomputed
+//              (stream, KV head) pairs and their split length.
+// scratch    -- the per-GPU device array of the no-allocation step.
 //
-// Layout of one bf16 LDS stage (64 keys, head_dim D):
-//   K tile  [64 keys][D]   row = 2D bytes, 16-byte slot c of key t stored at
-//                          slot c ^ (t & 7)
-//   V^T tile [D][64 keys]  row = 128 bytes; keys stored in the order in which
-//                          the score MFMA leaves P in registers, 16-byte slot s
-//                          of row d stored at s ^ ((d ^ (d >> 3)) & 7)
-// The XOR swizzles keep the 16-byte LDS reads of the MFMA operands and the
-// 16-byte writes of the staging threads free of bank conflicts.
+// Layout of one bf16 LDS stage (64 keys, head_dim D): the K tile, then the V
+// tile, each row-major [64 keys][D] (row = 2D bytes) as the direct-to-LDS
+// loads write them.  Both use one XOR swizzle of 16-byte slots: slot c of key
+// t is stored at c ^ 2*(t & 7) (D = 128; c ^ 2*(t & 3) at D = 64), even
+// values only, so the two slots of one 16-dim column block stay adjacent for
+// the transpose reads.  K fragments are read with 16-byte LDS reads, V^T
+// fragments with ds_read_b64_tr_b16; the counters read no bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1346,10 +1349,9 @@ __device__ __forceinline__ void tau_flag_token(const TauArgs& t, int64_t tok, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (e0 + u * 64 < nvec) {
-        const T* ka = (const T*)&a[u];
-        const T* kb = (const T*)&p[u];
-        const T* va = (const T*)&c[u];
-        const T* vb = (const T*)&q[u];
+        typedef T Vec __attribute__((ext_vector_type(VE)));   // the 16 bytes as VE elements
+        const Vec ka = __builtin_bit_cast(Vec, a[u]), kb = __builtin_bit_cast(Vec, p[u]);
+        const Vec va = __builtin_bit_cast(Vec, c[u]), vb = __builtin_bit_cast(Vec, q[u]);
 #pragma unroll
         for (int j = 0; j < VE; ++j) {
           const float dk = fabsf((float)ka[j] - (float)kb[j]);
