@@ -154,25 +154,27 @@ def test_big_block_ragged_streams(hq, hkv, lb, mode):
 
 
 @pytest.mark.parametrize("r", [1, 2])
-def test_sparse_chunk128_ragged_batch(r):
-    """128-token chunks (two 64-key tiles each) over two ragged streams whose
-    last chunks are partial; GQA 8/2, block 16."""
-    w = wl.Workload("sp128", "bf16", 2, 8, 2, 128, 16, 1500, 3, 0.5, 0.05, ragged=0.3, seed=91,
-                    sparse_keep=0.25, chunk_len=128)
+@pytest.mark.parametrize("chunk_len,d,lb", [(128, 128, 16), (64, 64, 48)], ids=["c128_d128", "c64_d64_192rows"])
+def test_sparse_chunk128_ragged_batch(r, chunk_len, d, lb):
+    """128-token chunks (two 64-key tiles each), and 64-token chunks at
+    head_dim 64 with 192 query rows per KV head (one 256-row prefix tile),
+    over two ragged streams whose last chunks are partial; GQA 8/2."""
+    w = wl.Workload("sp128", "bf16", 2, 8, 2, d, lb, 1500, 3, 0.5, 0.05, ragged=0.3, seed=91,
+                    sparse_keep=0.25, chunk_len=chunk_len)
     prefix, blocks = wl.make_inputs(w)
     chunks = wl.make_chunk_selection(w, prefix.lengths)
-    assert chunks.shape[-1] >= 2 and all(l % 128 for l in prefix.lengths)
+    assert chunks.shape[-1] >= 2 and all(l % chunk_len for l in prefix.lengths)
     for b in range(w.batch):   # include each stream's partial last chunk
-        last = (prefix.lengths[b] - 1) // 128
+        last = (prefix.lengths[b] - 1) // chunk_len
         for g in range(w.hkv):
             if last not in chunks[b, g]:
                 chunks[b, g, -1] = last
                 chunks[b, g] = np.sort(chunks[b, g])
     scale = scale_of(w)
     ref = oracle.run_block(prefix.k, prefix.v, prefix.offsets, blocks[0].q, blocks[0].k, blocks[0].v, scale, r=r,
-                           chunks=chunks, chunk_len=128)
+                           chunks=chunks, chunk_len=chunk_len)
     st = AttentionStep(w.dtype, w.batch, w.hq, w.hkv, w.head_dim, w.block_len, prefix.offsets,
-                       chunks=torch.from_numpy(chunks), chunk_len=128)
+                       chunks=torch.from_numpy(chunks), chunk_len=chunk_len)
     got = run_gpu(w, prefix, blocks[0], r, "cached", st=st)
     for s in range(w.steps):
         err = np.abs(got.out[s] - ref.out[s]).max()
