@@ -245,28 +245,39 @@ def test_edge_shapes(dtype, case):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_score_jump_reruns_pass(dtype):
+@pytest.mark.parametrize("shape", [
+    dict(hq=2, hkv=1, lb=100),   # 200 rows per KV head: the 8-wave 256-row split-KV pass; 2-tile block
+    dict(hq=2, hkv=1, lb=64),    # 128 rows: two 4-wave 128-row workgroups per CU
+    dict(hq=1, hkv=1, lb=32),    # 32 rows: the pipelined 16-row split-KV pass
+], ids=["rows200", "rows128", "rows32"])
+def test_score_jump_reruns_pass(dtype, shape):
     """Scores far above a pass's first-tile maxima (the kernel's softmax reference).
 
-    Prefix: 6 tiles, split as tiles 0-3 and 4-5 for 200 rows per KV head; a
-    large key in tile 3 and one in tile 5 give some rows scores more than 64
-    log2 units above their split's first-tile maxima, which sends the bf16
-    pass through its rerun against the split's exact maxima.  Block: the same
-    in its second tile (key 80 of 100).  Results must still match the oracle.
+    Prefix: 6 tiles, split as tiles 0-3 and 4-5 (splits of at least 4 tiles);
+    a large key in tile 3 and one in tile 5 give some rows scores more than
+    64 log2 units above their split's first-tile maxima, which sends the bf16
+    pass through its rerun against the split's exact maxima, from each
+    split-KV layout's own main loop.  Block (when it has a second tile): the
+    same in its second tile (key 80).  Results must still match the oracle.
     """
-    w, prefix, blk = _custom(dtype, batch=1, hq=2, hkv=1, d=128, lb=100, lens=[64 * 6])
+    lb = shape["lb"]
+    w, prefix, blk = _custom(dtype, batch=1, hq=shape["hq"], hkv=shape["hkv"], d=128, lb=lb, lens=[64 * 6])
     prefix.k[200] = 80.0
     prefix.k[330] = 80.0
-    blk.k[:, :, 80] = 80.0
+    if lb > 80:
+        blk.k[:, :, 80] = 80.0
     # precondition: some row's spike score clears its first tile's max by > 64 (log2)
     scale, log2e = scale_of(w), 1.0 / math.log(2.0)
     q = blk.q.astype(np.float64).reshape(-1, w.head_dim)
-    first = (q @ prefix.k[0:64, 0].astype(np.float64).T).max(axis=1)
-    spike = q @ prefix.k[200, 0].astype(np.float64)
-    assert ((spike - first) * scale * log2e > 64).any()
-    bfirst = np.einsum("sbthd,sbkd->sbthk", blk.q.astype(np.float64), blk.k[:, :, 0:64, 0].astype(np.float64)).max(-1)
-    bspike = np.einsum("sbthd,sbd->sbth", blk.q.astype(np.float64), blk.k[:, :, 80, 0].astype(np.float64))
-    assert ((bspike - bfirst) * scale * log2e > 64).any()
+    for spike_tok, first_tile in ((200, 0), (330, 4)):
+        first = (q @ prefix.k[64 * first_tile:64 * first_tile + 64, 0].astype(np.float64).T).max(axis=1)
+        spike = q @ prefix.k[spike_tok, 0].astype(np.float64)
+        assert ((spike - first) * scale * log2e > 64).any()
+    if lb > 80:
+        bfirst = np.einsum("sbthd,sbkd->sbthk", blk.q.astype(np.float64),
+                           blk.k[:, :, 0:64, 0].astype(np.float64)).max(-1)
+        bspike = np.einsum("sbthd,sbd->sbth", blk.q.astype(np.float64), blk.k[:, :, 80, 0].astype(np.float64))
+        assert ((bspike - bfirst) * scale * log2e > 64).any()
     for r, mode in ((1, "cached"), (2, "cached"), (1, "full")):
         check_block(w, prefix, blk, r, mode)
 
