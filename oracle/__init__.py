@@ -27,9 +27,11 @@ selected (the library routine over the whole prefix) and none (over the block
 alone), and by brute force over the selected tokens.  The block append is pinned against
 direct concatenation, and chunk selection by constructed pooled means, the
 max over a KV group's queries, ties to the lower index and a brute-force
-check of the kept set.  Cached mode at r > 1 is an
-approximation the pages define only as a procedure: its values are pinned only
-through those building blocks ("parity unpinned" for the drift values).
+check of the kept set.  Cached mode at r > 1, the sparse residual and the policies'
+per-head reuse are pinned by their closed form: one softmax over all keys in
+which each prefix key is scored against the query of the step that last
+refreshed it and each block (or selected-chunk) key against the current query,
+written out by brute force.
 """
 from .attention import (  # noqa: F401
     NEG_INF,

@@ -33,6 +33,13 @@ MUTATIONS = {
     "gqa_modulo": ("attention.py", "return h // (hq // hkv)", "return h % hkv"),
     "refresh_phase": ("attention.py", 'return mode == "full" or step % r == 0',
                       'return mode == "full" or step % r == r - 1'),
+    # the kept partials of a reuse step: the residual scored with the current
+    # queries, and heads a mask does not recompute refreshed anyway
+    "sparse_residual_current_queries": ("attention.py", "ext_o, ext_l = merge(cache_o, cache_l, sel_o, sel_l)",
+                                        "ext_o, ext_l = merge(*prefix_partial(q, k_pre, v_pre, offsets, scale, "
+                                        'chunks, chunk_len, "complement"), sel_o, sel_l)'),
+    "policy_refreshes_unmasked": ("policies.py", "if mask[b, kv_group(h, hq, hkv)]:\n                        cache_o",
+                                  "if True:\n                        cache_o"),
     # sparse token sets
     "complement_loses_token": ("attention.py", "return np.nonzero(~sel)[0]",
                                "return np.nonzero(~sel)[0][:-1]"),

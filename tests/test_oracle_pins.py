@@ -7,7 +7,10 @@
 * closed forms and invariants: zero keys, constant values, a single key, a
   constant shift of every score, key permutations, the partition invariant of
   the merge equation, r = 1 cached mode against full recompute, and the
-  refresh schedule.
+  refresh schedule;
+* cached mode at r > 1 (dense, sparse, per-head masks) in closed form: one
+  softmax in which prefix keys meet the refreshing step's queries and block
+  keys the current ones, written out by brute force.
 Each is chosen so that a plausible slip (a dropped scale or max term, a sign, a
 transposed operand, a wrong head mapping, a wrong refresh test) fails it.
 """
@@ -345,6 +348,115 @@ def test_refresh_schedule_and_drift():
     f2 = oracle.run_block(p.k, p.v, p.offsets, frozen, fk, fv, scale, mode="full")
     for s in range(5):
         np.testing.assert_allclose(c2.out[s], f2.out[s], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# cached mode at r > 1 in closed form
+# ---------------------------------------------------------------------------
+#
+# A reuse step merges the kept block-external partial (computed from the
+# queries of the step that last refreshed it) with a fresh block-internal
+# partial.  The merge is exact, so the output is one softmax over all keys in
+# which every prefix key is scored against the refreshing step's query and
+# every block key against the current query.  The brute force below writes
+# that softmax out with loops, without partials or the merge equation.
+
+def _brute_mixed(parts, scale):
+    """One softmax over several key sets, each set scored against its own
+    query: parts = [(query [D], keys [n][D], values [n][D]), ...]."""
+    scores, vals = [], []
+    for qv, ks, vs in parts:
+        qs = qv.tolist()
+        for kt, vt in zip(ks.tolist(), vs.tolist()):
+            scores.append(scale * sum(a * b for a, b in zip(qs, kt)))
+            vals.append(vt)
+    m = max(scores)
+    z = sum(math.exp(x - m) for x in scores)
+    out = [sum(math.exp(x - m) * v[j] for x, v in zip(scores, vals)) / z for j in range(len(vals[0]))]
+    return np.array(out), m + math.log(z)
+
+
+def _mixed_inputs(seed, lens, steps, hq=4, hkv=2, d=4, lb=3):
+    rng = np.random.default_rng(seed)
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    k_pre, v_pre = _rand(rng, int(offsets[-1]), hkv, d), _rand(rng, int(offsets[-1]), hkv, d)
+    b_n = len(lens)
+    q = [_rand(rng, b_n, lb, hq, d) for _ in range(steps)]
+    kb = [_rand(rng, b_n, lb, hkv, d) for _ in range(steps)]
+    vb = [_rand(rng, b_n, lb, hkv, d) for _ in range(steps)]
+    return offsets, k_pre, v_pre, q, kb, vb
+
+
+def _check_mixed(res, offsets, k_pre, v_pre, q, kb, vb, scale, prefix_parts):
+    """prefix_parts(s, b, g) -> [(step whose query scores them, token indices)]"""
+    b_n, lb, hq, _ = q[0].shape
+    hkv = kb[0].shape[2]
+    for s in range(len(q)):
+        for b in range(b_n):
+            t0 = int(offsets[b])
+            for h in range(hq):
+                g = h // (hq // hkv)
+                for i in range(lb):
+                    parts = [(q[sq][b, i, h], k_pre[t0 + toks, g], v_pre[t0 + toks, g])
+                             for sq, toks in prefix_parts(s, b, g) if len(toks)]
+                    parts.append((q[s][b, i, h], kb[s][b, :, g], vb[s][b, :, g]))
+                    bo, bl = _brute_mixed(parts, scale)
+                    np.testing.assert_allclose(res.out[s][b, i, h], bo, rtol=0, atol=1e-12)
+                    assert abs(res.lse[s][b, h, i] - bl) < 1e-12
+
+
+@pytest.mark.parametrize("r", [2, 3])
+def test_cached_mode_is_one_softmax_with_the_refresh_queries(r):
+    """Dense cached mode: prefix keys scored against the queries of step
+    r * floor(s / r), block keys against step s's (ragged GQA streams, one
+    prefix shorter than the block).  The drift against full recompute is the
+    difference of two pinned values."""
+    offsets, k_pre, v_pre, q, kb, vb = _mixed_inputs(31, [7, 2], steps=6)
+    scale = 0.45
+    res = oracle.run_block(k_pre, v_pre, offsets, q, kb, vb, scale, r=r)
+    lens = np.diff(offsets)
+    _check_mixed(res, offsets, k_pre, v_pre, q, kb, vb, scale,
+                 lambda s, b, g: [(r * (s // r), np.arange(lens[b]))])
+
+
+def test_sparse_cached_mode_is_one_softmax_with_the_refresh_queries():
+    """Sparse cached mode: the unselected chunks (the residual) scored against
+    the refreshing step's queries, the selected chunks and the block against
+    the current ones (2-token chunks, a ragged last chunk, per-KV-head lists,
+    a stream whose selection leaves no residual)."""
+    r, cl = 3, 2
+    offsets, k_pre, v_pre, q, kb, vb = _mixed_inputs(32, [7, 4], steps=5)
+    chunks = np.array([[[0, 3], [1, 2]], [[0, 1], [0, 1]]], dtype=np.int32)
+    scale = 0.5
+    res = oracle.run_block(k_pre, v_pre, offsets, q, kb, vb, scale, r=r, chunks=chunks, chunk_len=cl)
+    lens = np.diff(offsets)
+
+    def parts(s, b, g):
+        sel = sorted(t for c in chunks[b][g].tolist() for t in range(c * cl, min((c + 1) * cl, lens[b])))
+        rest = [t for t in range(lens[b]) if t not in sel]
+        return [(r * (s // r), np.array(rest, dtype=np.int64)), (s, np.array(sel, dtype=np.int64))]
+    _check_mixed(res, offsets, k_pre, v_pre, q, kb, vb, scale, parts)
+
+
+def test_policy_masks_are_one_softmax_with_each_heads_refresh_queries():
+    """Per-(stream, KV head) reuse (the τ and γ policies' given masks): the
+    prefix keys of a KV head scored against the queries of the last step
+    whose mask recomputed that head."""
+    steps = 6
+    offsets, k_pre, v_pre, q, kb, vb = _mixed_inputs(33, [5, 3], steps=steps)
+    rng = np.random.default_rng(34)
+    masks = [np.ones((2, 2), dtype=np.int32)] + [rng.integers(0, 2, (2, 2)).astype(np.int32)
+                                                 for _ in range(steps - 1)]
+    masks[3][:] = 0                      # a step that recomputes nothing
+    scale = 0.4
+    res = oracle.run_block_policy(k_pre, v_pre, offsets, q, kb, vb, scale, "given", masks=masks)
+    lens = np.diff(offsets)
+
+    def parts(s, b, g):
+        last = max(sp for sp in range(s + 1) if masks[sp][b, g])
+        return [(last, np.arange(lens[b]))]
+    _check_mixed(res, offsets, k_pre, v_pre, q, kb, vb, scale, parts)
+    assert any(masks[s][b, g] == 0 for s in range(1, steps) for b in range(2) for g in range(2))
 
 
 def test_refresh_due_rejects_bad_args():
