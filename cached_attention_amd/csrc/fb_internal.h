@@ -16,20 +16,23 @@ constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
 // faulted on MI355X).  X(id, rows per wave / 16, waves, LDS stages,
 // resident workgroups per CU, pass: 1 = split partial of the prefix pass,
 // 0 = block pass with merge, row waves: the first this many waves hold query
-// rows, the others only issue their share of the tile loads).  Query rows
-// per workgroup = row waves * 16 * (rows per wave / 16).
+// rows, the others only issue their share of the tile loads, key groups:
+// 1, or 2 = the row waves form two groups over the same rows, each taking
+// one 32-key half of every tile, merged through LDS at the end).  Query rows
+// per workgroup = row waves / key groups * 16 * (rows per wave / 16).
 #define FB_BF16_CFGS(X)                                                \
-  X(4, 1, 4, 2, 2, 0, 4)      /* block   64 rows                          */ \
-  X(5, 1, 8, 2, 1, 0, 8)      /* block  128 rows                          */ \
-  X(7, 2, 4, 2, 2, 1, 4)      /* prefix 128 rows, 2 workgroups per CU     */ \
-  X(9, 1, 2, 2, 2, 1, 2)      /* prefix  32 rows, 2 workgroups per CU     */ \
-  X(10, 1, 4, 2, 2, 1, 4)     /* prefix  64 rows, 2 workgroups per CU     */ \
-  X(18, 2, 8, 2, 1, 0, 8)     /* block  256 rows: 8 waves x 32            */ \
-  X(19, 2, 4, 2, 2, 0, 4)     /* block  128 rows, 2 workgroups per CU     */ \
-  X(21, 1, 2, 2, 2, 0, 2)     /* block   32 rows: 2 waves x 16            */ \
-  X(22, 1, 4, 2, 2, 0, 2)     /* block   32 rows + 2 loading waves        */ \
-  X(26, 1, 4, 2, 2, 0, 1)     /* block   16 rows + 3 loading waves        */ \
-  X(27, 2, 8, 2, 1, 1, 8)     /* prefix 256 rows: 8 waves x 32            */
+  X(4, 1, 4, 2, 2, 0, 4, 1)      /* block   64 rows                          */ \
+  X(5, 1, 8, 2, 1, 0, 8, 1)      /* block  128 rows                          */ \
+  X(7, 2, 4, 2, 2, 1, 4, 1)      /* prefix 128 rows, 2 workgroups per CU     */ \
+  X(9, 1, 2, 2, 2, 1, 2, 1)      /* prefix  32 rows, 2 workgroups per CU     */ \
+  X(10, 1, 4, 2, 2, 1, 4, 1)     /* prefix  64 rows, 2 workgroups per CU     */ \
+  X(18, 2, 8, 2, 1, 0, 8, 1)     /* block  256 rows: 8 waves x 32            */ \
+  X(19, 2, 4, 2, 2, 0, 4, 1)     /* block  128 rows, 2 workgroups per CU     */ \
+  X(21, 1, 2, 2, 2, 0, 2, 1)     /* block   32 rows: 2 waves x 16            */ \
+  X(22, 1, 4, 2, 2, 0, 2, 1)     /* block   32 rows + 2 loading waves        */ \
+  X(26, 1, 4, 2, 2, 0, 1, 1)     /* block   16 rows + 3 loading waves        */ \
+  X(27, 2, 8, 2, 1, 1, 8, 1)     /* prefix 256 rows: 8 waves x 32            */ \
+  X(29, 2, 4, 2, 2, 0, 4, 2)     /* block   64 rows: 2 x 32 rows x 2 key halves */
 
 enum KernelCfg : int32_t {
   CFG_B64 = 4,
@@ -43,6 +46,7 @@ enum KernelCfg : int32_t {
   CFG_B32_LD = 22,
   CFG_B16_LD = 26,
   CFG_P256 = 27,
+  CFG_B64_K2 = 29,
 };
 
 struct CfgInfo {
@@ -51,8 +55,8 @@ struct CfgInfo {
 };
 inline CfgInfo cfg_info(int cfg) {
   switch (cfg) {
-#define FB_CFG_INFO(ID, QT, NW, NS, WPC, PART, RW) \
-    case ID: return {(RW) * 16 * (QT), WPC};
+#define FB_CFG_INFO(ID, QT, NW, NS, WPC, PART, RW, KG) \
+    case ID: return {(RW) / (KG) * 16 * (QT), WPC};
     FB_BF16_CFGS(FB_CFG_INFO)
 #undef FB_CFG_INFO
     default: return {64, 1};

@@ -35,6 +35,9 @@
 // values only, so the two slots of one 16-dim column block stay adjacent for
 // the transpose reads.  K fragments are read with 16-byte LDS reads, V^T
 // fragments with ds_read_b64_tr_b16; the counters read no bank conflicts.
+// Block passes of 1024 rows and more per KV head split every tile between two
+// key groups of waves (keys 0..31 and 32..63); after the last tile the ring
+// holds group 1's (O, m, l) for group 0 to merge.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -251,8 +254,11 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
 //
 // Workgroup: NW waves; wave w < RW owns 16*QT consecutive query rows of one KV
 // head (row i -> query head g*G + i / Lb, block position i % Lb); waves RW ..
-// NW-1 hold no rows and only issue their share of the tile loads.  Per
-// 64-key tile:
+// NW-1 hold no rows and only issue their share of the tile loads.  With KG = 2
+// key groups (block pass only) waves w and w + NW/2 own the same rows, the
+// first taking keys 0..31 of every tile and the second keys 32..63; each
+// group keeps its own softmax reference, and the two partials are merged
+// through LDS before the epilogue.  Per 64-key tile (per 32-key half):
 //   S^T[key][q] = K Q^T      v_mfma_f32_16x16x32_bf16, A = K from LDS,
 //                            B = Q^T held in VGPRs for the whole pass
 //   online softmax on S^T    each lane holds one query column (lane & 15) and
@@ -391,13 +397,17 @@ __device__ __forceinline__ void mfma_prio() {
   if constexpr (FB_MFMA_PRIO != 0) __builtin_amdgcn_s_setprio(P);
 }
 
-template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL, int RW>
+template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL, int RW, int KG>
 __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the score MFMA
   constexpr int DT = D / 16;                  // 16-row d tiles of O^T
   constexpr int CH = D / 8;                   // 16-byte slots per key row
-  constexpr int ROWS = RW * 16 * QT;          // query rows per workgroup (waves 0 .. RW-1)
+  constexpr int RWG = RW / KG;                // row waves per key group
+  constexpr int ROWS = RWG * 16 * QT;         // query rows per workgroup
+  constexpr int TT = 4 / KG;                  // 16-key groups of a tile each wave takes
+  constexpr int PH = TT / 2;                  // 32-key halves of a tile each wave takes
   static_assert(RW >= 1 && RW <= NW, "row waves");
+  static_assert(KG == 1 || (KG == 2 && RW == NW && !PARTIAL), "key groups: block pass, every wave a row wave");
   constexpr int kVAhead = v_ahead<QT>();
   constexpr int kKAhead = k_ahead<QT>();
   constexpr int TBYTES = kTile * D * 2;       // one K or V tile
@@ -406,7 +416,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int IPW = 2 * IPT / NW;           // loads per wave per tile
   constexpr int RPI = 1024 / (2 * D);         // key rows per load instruction
   constexpr int DIST = NS - 1;                // prefetch distance in tiles
-  constexpr int NG = 2 * DT;                  // MFMA groups of the PV product
+  constexpr int NG = PH * DT;                 // MFMA groups of the PV product
   static_assert(IPT % IPW == 0 && IPW % 2 == 0, "each wave loads an even run of one tensor");
   static_assert(NS >= 2 && NS <= 4, "2..4 stages");
   // The direct-to-LDS loads address LDS through M0.  Rings reaching 64 KB and
@@ -425,10 +435,15 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // key group of the wave (wave-uniform): group kg takes keys kofs .. kofs +
+  // 64/KG - 1 of every tile; wr = the wave's row slot within its group
+  const int kg = KG == 1 ? 0 : wave / (NW / KG);
+  const int wr = wave - kg * (NW / KG);
+  const int kofs = kg * (kTile / KG);
 
   // ---- query fragments (B operand of the score MFMA) ----
-  const int row_w0 = wk.rt * ROWS + wave * 16 * QT;
-  const bool row_wave = wave < RW;            // waves RW .. NW-1 only load tiles
+  const int row_w0 = wk.rt * ROWS + wr * 16 * QT;
+  const bool row_wave = wr < RWG;             // waves RW .. NW-1 only load tiles
   const bool wave_active = row_wave && row_w0 < a.rows;
   bf16x8 qf[QT][KS];
 #pragma unroll
@@ -531,14 +546,14 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // (l16 >> 2), dims 16*dt + 4*(l16 & 3), swizzled)
   uint32_t koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = l16 * (2 * D) + (((ks * 4 + lg) ^ kv_swz<D>(l16)) * 16);
-  const uint32_t vlane = (4 * lg + (l16 >> 2)) * (2 * D) + 8 * (l16 & 3);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = (kofs + l16) * (2 * D) + (((ks * 4 + lg) ^ kv_swz<D>(l16)) * 16);
+  const uint32_t vlane = (kofs + 4 * lg + (l16 >> 2)) * (2 * D) + 8 * (l16 & 3);
   const int vkx = kv_swz<D>(4 * lg + (l16 >> 2)) >> 1;
 
-  f32x4 s[4][QT];
+  f32x4 s[TT][QT];
   // V^T fragments of the deferred PV groups; their P^T operands stay in pf
   bf16x8 vdef[kPvDefer > 0 ? kPvDefer : 1];
-  bf16x8 pf[2][QT];
+  bf16x8 pf[PH][QT];
   auto run_deferred = [&]() __attribute__((always_inline)) {
     if constexpr (kPvDefer > 0) {
       mfma_prio<1>();
@@ -558,11 +573,11 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   // fragments of step ks+1 are read while the MFMAs of step ks run; the
   // scheduling fences keep the compiler from sinking the reads next to
   // their MFMAs, where each group would wait out the LDS latency.
-  bf16x8 kf[KS][4];   // keys 16*tt + l16, 16-byte slot 4*ks + lg
+  bf16x8 kf[KS][TT];   // keys kofs + 16*tt + l16, 16-byte slot 4*ks + lg
   auto kload = [&](uint32_t kb, int ks) __attribute__((always_inline)) {
     const FB_LDS char* kp = (const FB_LDS char*)(uintptr_t)(kb + koff[ks]);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
+    for (int tt = 0; tt < TT; ++tt) kf[ks][tt] = *(const FB_LDS bf16x8*)(kp + tt * 16 * 2 * D);
   };
   // the first K reads of a tile, issued as early as possible after its barrier
   auto scores_begin = [&](uint32_t kb) __attribute__((always_inline)) {
@@ -571,7 +586,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   };
   auto scores = [&](uint32_t kb, auto pend_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) s[tt][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if constexpr (decltype(pend_tag)::value != 0) {   // the previous tile's last PV groups cover the K reads
@@ -585,7 +600,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       if (ks + kKAhead < KS) kload(kb, ks + kKAhead);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           s[tt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], qf[qt][ks], s[tt][qt], 0, 0, 0);
@@ -598,7 +613,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   auto row_max = [&](int qt) __attribute__((always_inline)) {
     float mx = kNegInf;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt][i]);
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -614,9 +629,9 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float msub = m_run[qt] == kNegInf ? 0.f : m_run[qt];
-      uint32_t pk[4][2];
+      uint32_t pk[TT][2];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
+      for (int tt = 0; tt < TT; ++tt) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][qt][i], c, -msub));
@@ -624,12 +639,12 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
         pk[tt][1] = pack_bf16x2(p[2], p[3]);
       }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           l_run[qt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[tt][h]), ones2, l_run[qt], false);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+      for (int jj = 0; jj < PH; ++jj) {
         u32x4 pv = {pk[2 * jj][0], pk[2 * jj][1], pk[2 * jj + 1][0], pk[2 * jj + 1][1]};
         pf[jj][qt] = __builtin_bit_cast(bf16x8, pv);
       }
@@ -645,7 +660,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   auto softmax_pv = [&](uint32_t vb, int nvalid, auto mode_tag) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_tag)::value;
-    bf16x8 vf[NG];
+    bf16x8 vf[NG > 0 ? NG : 1];
     auto vload = [&](int g) __attribute__((always_inline)) {
       const int jj = g / DT, dt = g % DT;
       const uint32_t va = vb + vlane + 32 * (dt ^ vkx) + jj * 32 * 2 * D;
@@ -660,10 +675,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
     if (nvalid < kTile) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool dead = tt * 16 + 4 * lg + i >= nvalid;
+          const bool dead = kofs + tt * 16 + 4 * lg + i >= nvalid;
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
             if (dead) s[tt][qt][i] = kNegInf;
@@ -673,7 +688,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx_lane[qt] = fmaxf(mx_lane[qt], s[tt][qt][i]);
       return;
@@ -949,6 +964,38 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       wk.it = it0;
       run_pass(IC<0>{}, IC<0>{}, IC<0>{});
     }
+  }
+
+  // ---- two key groups: group 1 hands its (O, m, l) of each row to group 0
+  // through the (now idle) ring, one query sub-tile at a time; group 0 puts
+  // both on the larger of the two references and adds them ----
+  if constexpr (KG == 2) {
+    static_assert(RWG * DT * 64 * 16 + RWG * 64 * 8 <= NS * STAGE, "merge buffer within the ring");
+    f32x4* xo = (f32x4*)smem;                                   // [RWG][DT][64 lanes]
+    float2* xs = (float2*)(smem + RWG * DT * 64 * 16);          // [RWG][64 lanes]: (m, l)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      __syncthreads();   // every wave is done with the ring (its last tile, or the previous sub-tile)
+      if (wave_active && kg == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xo[(wr * DT + dt) * 64 + lane] = oacc[dt][qt];
+        xs[wr * 64 + lane] = make_float2(m_run[qt], l_run[qt]);
+      }
+      __syncthreads();
+      if (wave_active && kg == 0) {
+        const float2 ml = xs[wr * 64 + lane];
+        const float mm = fmaxf(m_run[qt], ml.x);
+        // log2-domain references; a group whose keys all fell past the end
+        // (reference -inf, zero sum) gets weight 0
+        const float a0 = m_run[qt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mm);
+        const float a1 = ml.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml.x - mm);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = oacc[dt][qt] * a0 + xo[(wr * DT + dt) * 64 + lane] * a1;
+        l_run[qt] = l_run[qt] * a0 + ml.y * a1;
+        m_run[qt] = mm;
+      }
+    }
+    if (kg != 0) return;
   }
 
   if (!wave_active) return;
@@ -2054,10 +2101,10 @@ int noalloc_scratch(void** ptr) {
 constexpr int64_t kMaxBlocks = 1 << 20;
 static dim3 capped_grid(int64_t blocks) { return dim3((unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks)); }
 
-template <int D, int QT, int NW, int NS, int WPC, bool P, int RW>
+template <int D, int QT, int NW, int NS, int WPC, bool P, int RW, int KG>
 static int launch_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int minw = (NW * WPC + 3) / 4;   // waves per SIMD when WPC workgroups share a CU
-  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, minw, P, RW>), dim3(a.grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((attn_bf16<D, QT, NW, NS, minw, P, RW, KG>), dim3(a.grid), dim3(64 * NW), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -2070,8 +2117,8 @@ static int launch_f32(const AttnArgs& a, hipStream_t s) {
 template <int D>
 static int launch_bf16_cfg(const AttnArgs& a, int cfg, hipStream_t s) {
   switch (cfg) {
-#define FB_CFG_LAUNCH(ID, QT, NW, NS, WPC, PART, RW) \
-    case ID: return launch_bf16<D, QT, NW, NS, WPC, (PART) != 0, RW>(a, s);
+#define FB_CFG_LAUNCH(ID, QT, NW, NS, WPC, PART, RW, KG) \
+    case ID: return launch_bf16<D, QT, NW, NS, WPC, (PART) != 0, RW, KG>(a, s);
     FB_BF16_CFGS(FB_CFG_LAUNCH)
 #undef FB_CFG_LAUNCH
     default: return (int)hipErrorInvalidValue;

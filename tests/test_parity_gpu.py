@@ -249,7 +249,8 @@ def test_edge_shapes(dtype, case):
     dict(hq=2, hkv=1, lb=100),   # 200 rows per KV head: the 8-wave 256-row split-KV pass; 2-tile block
     dict(hq=2, hkv=1, lb=64),    # 128 rows: two 4-wave 128-row workgroups per CU
     dict(hq=1, hkv=1, lb=32),    # 32 rows: the pipelined 16-row split-KV pass
-], ids=["rows200", "rows128", "rows32"])
+    dict(hq=1, hkv=1, lb=1100),  # 1100 rows: the block pass's two key groups, a spike in each one's half
+], ids=["rows200", "rows128", "rows32", "rows1100"])
 def test_score_jump_reruns_pass(dtype, shape):
     """Scores far above a pass's first-tile maxima (the kernel's softmax reference).
 
@@ -258,14 +259,17 @@ def test_score_jump_reruns_pass(dtype, shape):
     64 log2 units above their split's first-tile maxima, which sends the bf16
     pass through its rerun against the split's exact maxima, from each
     split-KV layout's own main loop.  Block (when it has a second tile): the
-    same in its second tile (key 80).  Results must still match the oracle.
+    same in its second tile (key 80), and for blocks of 1024 rows and more,
+    whose waves split every tile into two 32-key halves, also in the second
+    half of its third tile (key 168).  Results must still match the oracle.
     """
     lb = shape["lb"]
     w, prefix, blk = _custom(dtype, batch=1, hq=shape["hq"], hkv=shape["hkv"], d=128, lb=lb, lens=[64 * 6])
     prefix.k[200] = 80.0
     prefix.k[330] = 80.0
-    if lb > 80:
-        blk.k[:, :, 80] = 80.0
+    spikes = [t for t in (80, 168) if t < lb and (t == 80 or lb >= 1024)]
+    for t in spikes:
+        blk.k[:, :, t] = 80.0
     # precondition: some row's spike score clears its first tile's max by > 64 (log2)
     scale, log2e = scale_of(w), 1.0 / math.log(2.0)
     q = blk.q.astype(np.float64).reshape(-1, w.head_dim)
@@ -273,10 +277,10 @@ def test_score_jump_reruns_pass(dtype, shape):
         first = (q @ prefix.k[64 * first_tile:64 * first_tile + 64, 0].astype(np.float64).T).max(axis=1)
         spike = q @ prefix.k[spike_tok, 0].astype(np.float64)
         assert ((spike - first) * scale * log2e > 64).any()
-    if lb > 80:
+    for t in spikes:
         bfirst = np.einsum("sbthd,sbkd->sbthk", blk.q.astype(np.float64),
                            blk.k[:, :, 0:64, 0].astype(np.float64)).max(-1)
-        bspike = np.einsum("sbthd,sbd->sbth", blk.q.astype(np.float64), blk.k[:, :, 80, 0].astype(np.float64))
+        bspike = np.einsum("sbthd,sbd->sbth", blk.q.astype(np.float64), blk.k[:, :, t, 0].astype(np.float64))
         assert ((bspike - bfirst) * scale * log2e > 64).any()
     for r, mode in ((1, "cached"), (2, "cached"), (1, "full")):
         check_block(w, prefix, blk, r, mode)
