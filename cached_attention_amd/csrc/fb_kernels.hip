@@ -966,36 +966,51 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     }
   }
 
-  // ---- two key groups: group 1 hands its (O, m, l) of each row to group 0
-  // through the (now idle) ring, one query sub-tile at a time; group 0 puts
-  // both on the larger of the two references and adds them ----
+  // ---- two key groups: each group finishes half of the head dims, group kg
+  // the d tiles [kg * DT/2, (kg + 1) * DT/2).  Through the (now idle) ring,
+  // one query sub-tile at a time, each wave hands the other group's half of
+  // its O and its (m, l) to its partner wave; both put the two partials on the
+  // larger reference and add them.  The epilogue's reads of the cached
+  // partial and writes of O are then spread over every wave. ----
+  constexpr int DH = KG == 2 ? DT / 2 : DT;   // d tiles each wave finishes
   if constexpr (KG == 2) {
-    static_assert(RWG * DT * 64 * 16 + RWG * 64 * 8 <= NS * STAGE, "merge buffer within the ring");
-    f32x4* xo = (f32x4*)smem;                                   // [RWG][DT][64 lanes]
-    float2* xs = (float2*)(smem + RWG * DT * 64 * 16);          // [RWG][64 lanes]: (m, l)
+    static_assert(KG * RWG * DH * 64 * 16 + KG * RWG * 64 * 8 <= NS * STAGE, "merge buffer within the ring");
+    f32x4* xo = (f32x4*)smem;                                   // [group][RWG][DH][64 lanes]
+    float2* xs = (float2*)(smem + KG * RWG * DH * 64 * 16);     // [group][RWG][64 lanes]: (m, l)
+    // the accumulators are indexed with compile-time d tiles only (a
+    // run-time index would move them to scratch memory): one instance per
+    // key group, chosen by the wave-uniform kg
+    auto exchange = [&](int qt, auto own_tag) __attribute__((always_inline)) {
+      constexpr int own = decltype(own_tag)::value, oth = 1 - own;
+#pragma unroll
+      for (int e = 0; e < DH; ++e) xo[((own * RWG + wr) * DH + e) * 64 + lane] = oacc[oth * DH + e][qt];
+      xs[(own * RWG + wr) * 64 + lane] = make_float2(m_run[qt], l_run[qt]);
+    };
+    auto merge_own = [&](int qt, auto own_tag) __attribute__((always_inline)) {
+      constexpr int own = decltype(own_tag)::value, oth = 1 - own;
+      const float2 ml = xs[(oth * RWG + wr) * 64 + lane];
+      const float mm = fmaxf(m_run[qt], ml.x);
+      // log2-domain references; a group whose keys all fell past the end
+      // (reference -inf, zero sum) gets weight 0
+      const float a0 = m_run[qt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mm);
+      const float a1 = ml.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml.x - mm);
+#pragma unroll
+      for (int e = 0; e < DH; ++e)
+        oacc[own * DH + e][qt] = oacc[own * DH + e][qt] * a0 + xo[((oth * RWG + wr) * DH + e) * 64 + lane] * a1;
+      l_run[qt] = l_run[qt] * a0 + ml.y * a1;
+      m_run[qt] = mm;
+    };
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       __syncthreads();   // every wave is done with the ring (its last tile, or the previous sub-tile)
-      if (wave_active && kg == 1) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xo[(wr * DT + dt) * 64 + lane] = oacc[dt][qt];
-        xs[wr * 64 + lane] = make_float2(m_run[qt], l_run[qt]);
+      if (wave_active) {
+        if (kg == 0) exchange(qt, IC<0>{}); else exchange(qt, IC<1>{});
       }
       __syncthreads();
-      if (wave_active && kg == 0) {
-        const float2 ml = xs[wr * 64 + lane];
-        const float mm = fmaxf(m_run[qt], ml.x);
-        // log2-domain references; a group whose keys all fell past the end
-        // (reference -inf, zero sum) gets weight 0
-        const float a0 = m_run[qt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - mm);
-        const float a1 = ml.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml.x - mm);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt][qt] = oacc[dt][qt] * a0 + xo[(wr * DT + dt) * 64 + lane] * a1;
-        l_run[qt] = l_run[qt] * a0 + ml.y * a1;
-        m_run[qt] = mm;
+      if (wave_active) {
+        if (kg == 0) merge_own(qt, IC<0>{}); else merge_own(qt, IC<1>{});
       }
     }
-    if (kg != 0) return;
   }
 
   if (!wave_active) return;
@@ -1033,18 +1048,25 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
       const float we_n = we * rden;
       __bf16* op = (__bf16*)a.o + (((int64_t)wk.b * a.Lb + pos) * a.Hq + h) * D + 4 * lg;
       const float* ep = a.ext_o ? a.ext_o + crow * D + 4 * lg : nullptr;
+      // the wave's d tiles: all of them, or its key group's half (compile-time
+      // tile indices, one instance per group)
+      auto store = [&](auto d0_tag) __attribute__((always_inline)) {
+        constexpr int d0 = decltype(d0_tag)::value;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 r = oacc[dt][qt] * wi_n;
-        if constexpr (kPre) {
-          r += ext_pre[qt][dt] * we_n;   // zeros when there is no cache
-        } else {
-          if (ep) r += *(const f32x4*)(ep + dt * 16) * we_n;
+        for (int e = 0; e < DH; ++e) {
+          const int dt = d0 + e;
+          f32x4 r = oacc[dt][qt] * wi_n;
+          if constexpr (kPre) {
+            r += ext_pre[qt][dt] * we_n;   // zeros when there is no cache
+          } else {
+            if (ep) r += *(const f32x4*)(ep + dt * 16) * we_n;
+          }
+          u32x2 packed = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+          *(u32x2*)(op + dt * 16) = packed;
         }
-        u32x2 packed = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
-        *(u32x2*)(op + dt * 16) = packed;
-      }
-      if (lg == 0 && a.lse_out) a.lse_out[crow] = mm + __logf(den);
+      };
+      if (KG == 1 || kg == 0) store(IC<0>{}); else store(IC<DH>{});
+      if (lg == 0 && kg == 0 && a.lse_out) a.lse_out[crow] = mm + __logf(den);
     }
   }
 }
