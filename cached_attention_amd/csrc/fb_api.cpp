@@ -79,15 +79,25 @@ int block_cfg(const fb_desc* d) {
   // build-time override (used to sweep configurations)
   return rows >= 1024 ? FB_BLOCK_CFG_BIG : FB_BLOCK_CFG_SMALL;
 #else
-  // measured on MI355X: blocks of 1024 rows and more per KV head (the
-  // 1560-row video frame) take 64-row workgroups of four 32-row waves in two
-  // key groups, two workgroups per CU, whose phases drift apart: 5% faster
-  // than eight 16-row waves on the video block, 12-20% on smaller big blocks.
+  // measured on MI355X: blocks of 1024 rows and more per KV head take
+  // workgroups in two key groups: 64 rows (four 32-row waves, two
+  // workgroups per CU, 12-20% faster than eight 16-row waves on small grids)
+  // or, for the 1560-row video frame, 80 rows (ten 16-row waves, one per
+  // CU: 25.3 against 31.1 us for eight 16-row waves, 29.8 for 64 rows).
   // Text blocks are latency-bound and run fastest on
   // 4-wave workgroups whose extra waves only issue tile loads: 16 rows (one
   // row wave) while that gives at most one workgroup per CU, else 32 rows
   // (two row waves), which beat 16-row ones once those fill the CUs twice.
-  if (rows >= 1024) return fb::CFG_B64_K2;
+  if (rows >= 1024) {
+    // 80-row workgroups of five 16-row waves in two key groups, one per CU,
+    // where the 64-row ones would leave some CUs with two (the 1560-row
+    // video frame: 300 workgroups of 64 rows, 240 of 80); the busiest SIMD
+    // then holds three 16-row waves over half the keys instead of two
+    // 32-row ones
+    const int64_t wgs64 = (int64_t)d->batch * d->hkv * ceil_div(rows, 64);
+    const int64_t wgs80 = (int64_t)d->batch * d->hkv * ceil_div(rows, 80);
+    return (wgs64 > kCUs && wgs80 <= kCUs) ? fb::CFG_B80_K2 : fb::CFG_B64_K2;
+  }
   const int64_t wgs16 = (int64_t)d->batch * d->hkv * ceil_div(rows, 16);
   return wgs16 <= kCUs ? fb::CFG_B16_LD : fb::CFG_B32_LD;
 #endif

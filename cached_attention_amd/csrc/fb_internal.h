@@ -32,7 +32,8 @@ constexpr int kDtypeBf16 = 1;  // FB_BF16 of the public header
   X(22, 1, 4, 2, 2, 0, 2, 1)     /* block   32 rows + 2 loading waves        */ \
   X(26, 1, 4, 2, 2, 0, 1, 1)     /* block   16 rows + 3 loading waves        */ \
   X(27, 2, 8, 2, 1, 1, 8, 1)     /* prefix 256 rows: 8 waves x 32            */ \
-  X(29, 2, 4, 2, 2, 0, 4, 2)     /* block   64 rows: 2 x 32 rows x 2 key halves */
+  X(29, 2, 4, 2, 2, 0, 4, 2)     /* block   64 rows: 2 x 32 rows x 2 key halves */ \
+  X(30, 1, 10, 2, 1, 0, 10, 2)   /* block   80 rows: 5 x 16 rows x 2 key halves */
 
 enum KernelCfg : int32_t {
   CFG_B64 = 4,
@@ -47,6 +48,7 @@ enum KernelCfg : int32_t {
   CFG_B16_LD = 26,
   CFG_P256 = 27,
   CFG_B64_K2 = 29,
+  CFG_B80_K2 = 30,
 };
 
 struct CfgInfo {

@@ -413,7 +413,8 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int TBYTES = kTile * D * 2;       // one K or V tile
   constexpr int STAGE = 2 * TBYTES;
   constexpr int IPT = TBYTES / 1024;          // 1 KB direct-to-LDS loads per tile and tensor
-  constexpr int IPW = 2 * IPT / NW;           // loads per wave per tile
+  constexpr int LW = NW > 8 ? 8 : NW;         // waves that issue the tile loads (the first LW)
+  constexpr int IPW = 2 * IPT / LW;           // loads per loading wave per tile
   constexpr int RPI = 1024 / (2 * D);         // key rows per load instruction
   constexpr int DIST = NS - 1;                // prefetch distance in tiles
   constexpr int NG = PH * DT;                 // MFMA groups of the PV product
@@ -507,13 +508,16 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   if (tid == 0) wg_redo = 0;
 
   // ---- direct-to-LDS tile loads ----
-  // Waves 0..NW/2-1 load K, the others V; wave w's IPW instructions cover the
-  // 1 KB chunks jj0 .. jj0+IPW-1 of its tensor's tile (RPI key rows each).
-  // Lane -> (key row, 16-byte slot); the slot swizzle is applied on the global
-  // side so each instruction writes one contiguous 1 KB block of LDS.  The
-  // per-lane part of the global offset depends only on the chunk parity.
-  const bool dma_v = wave >= NW / 2;
-  const int jj0 = (dma_v ? wave - NW / 2 : wave) * IPW;
+  // Waves 0..LW/2-1 load K, waves LW/2..LW-1 V (waves past LW, in the
+  // workgroups of more than 8 waves, load nothing); wave w's IPW instructions
+  // cover the 1 KB chunks jj0 .. jj0+IPW-1 of its tensor's tile (RPI key rows
+  // each).  Lane -> (key row, 16-byte slot); the slot swizzle is applied on
+  // the global side so each instruction writes one contiguous 1 KB block of
+  // LDS.  The per-lane part of the global offset depends only on the chunk
+  // parity.
+  const bool loader = wave < LW;
+  const bool dma_v = wave >= LW / 2;
+  const int jj0 = loader ? (dma_v ? wave - LW / 2 : wave) * IPW : 0;
   const char* gsrc = dma_v ? wk.vbase : wk.kbase;
   const uint32_t lds_dst = lds0 + (dma_v ? TBYTES : 0) + jj0 * 1024;
   const int64_t row_bytes = a.kv_st * 2;
@@ -524,6 +528,7 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
     lane_part[par] = (uint32_t)(row * row_bytes) + ((lane % CH) ^ kv_swz<D>(row)) * 16;
   }
   auto issue = [&](int stage, int64_t tok0, int nvalid) __attribute__((always_inline)) {
+    if (!loader) return;   // wave-uniform
     const char* g = gsrc + tok0 * row_bytes;
     const uint32_t dst = lds_dst + stage * STAGE;
     if (nvalid < kTile) {   // ragged tile: rows past the end re-read the last key (masked later)

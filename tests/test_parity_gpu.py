@@ -144,11 +144,14 @@ def test_text_gqa_sparse(r):
     check_block(w, prefix, blocks[0], r, "cached", chunks=chunks)
 
 
-@pytest.mark.parametrize("hq,hkv,lb,mode", [(2, 2, 1100, "cached"), (8, 2, 300, "cached"), (8, 2, 300, "full")])
-def test_big_block_ragged_streams(hq, hkv, lb, mode):
-    """Blocks of >= 1024 query rows per KV head (the 8-wave block configuration),
-    MHA and GQA, over two ragged streams, cached and full."""
-    w = wl.Workload("big", "bf16", 2, hq, hkv, 128, lb, 300, 3, 1.0, 0.1, ragged=0.25, seed=97)
+@pytest.mark.parametrize("batch,hq,hkv,lb,mode", [(2, 2, 2, 1100, "cached"), (2, 8, 2, 300, "cached"),
+                                                  (2, 8, 2, 300, "full"), (1, 16, 16, 1190, "cached")])
+def test_big_block_ragged_streams(batch, hq, hkv, lb, mode):
+    """Blocks of >= 1024 query rows per KV head (the key-group block
+    configurations), MHA and GQA, over ragged streams, cached and full.  The
+    16-head, 1190-token block needs 304 workgroups of 64 rows but 240 of 80,
+    so it runs the 80-row form (ragged in rows and in keys)."""
+    w = wl.Workload("big", "bf16", batch, hq, hkv, 128, lb, 300, 3, 1.0, 0.1, ragged=0.25, seed=97)
     prefix, blocks = wl.make_inputs(w)
     check_block(w, prefix, blocks[0], 2, mode)
 
@@ -250,7 +253,8 @@ def test_edge_shapes(dtype, case):
     dict(hq=2, hkv=1, lb=64),    # 128 rows: two 4-wave 128-row workgroups per CU
     dict(hq=1, hkv=1, lb=32),    # 32 rows: the pipelined 16-row split-KV pass
     dict(hq=1, hkv=1, lb=1100),  # 1100 rows: the block pass's two key groups, a spike in each one's half
-], ids=["rows200", "rows128", "rows32", "rows1100"])
+    dict(hq=16, hkv=16, lb=1190),  # 16 x 1190 rows: the 80-row key-group block workgroups
+], ids=["rows200", "rows128", "rows32", "rows1100", "heads16_rows1190"])
 def test_score_jump_reruns_pass(dtype, shape):
     """Scores far above a pass's first-tile maxima (the kernel's softmax reference).
 
