@@ -89,14 +89,15 @@ int block_cfg(const fb_desc* d) {
   // row wave) while that gives at most one workgroup per CU, else 32 rows
   // (two row waves), which beat 16-row ones once those fill the CUs twice.
   if (rows >= 1024) {
-    // 80-row workgroups of five 16-row waves in two key groups, one per CU,
-    // where the 64-row ones would leave some CUs with two (the 1560-row
-    // video frame: 300 workgroups of 64 rows, 240 of 80); the busiest SIMD
-    // then holds three 16-row waves over half the keys instead of two
-    // 32-row ones
+    // 80-row workgroups of ten 16-row waves in two key groups, one per CU,
+    // wherever the 64-row ones would leave some CUs with two or more (the
+    // 1560-row video frame: 300 workgroups of 64 rows, 240 of 80; two
+    // frames: 600 and 480, 49.3 against 53.6 us); the busiest SIMD then
+    // holds three 16-row waves over half the keys instead of two 32-row
+    // ones.  Grids of at most one 64-row workgroup per CU keep 64 rows
+    // (8 heads x 1560 rows: 24.1 against 24.5 us).
     const int64_t wgs64 = (int64_t)d->batch * d->hkv * ceil_div(rows, 64);
-    const int64_t wgs80 = (int64_t)d->batch * d->hkv * ceil_div(rows, 80);
-    return (wgs64 > kCUs && wgs80 <= kCUs) ? fb::CFG_B80_K2 : fb::CFG_B64_K2;
+    return wgs64 > kCUs ? fb::CFG_B80_K2 : fb::CFG_B64_K2;
   }
   const int64_t wgs16 = (int64_t)d->batch * d->hkv * ceil_div(rows, 16);
   return wgs16 <= kCUs ? fb::CFG_B16_LD : fb::CFG_B32_LD;
