@@ -75,29 +75,30 @@ int prefix_cfg(const fb_desc* d) {
 }
 int block_cfg(const fb_desc* d) {
   const int rows = (d->hq / d->hkv) * d->block_len;
+  const bool key_groups = rows >= 1024 || d->block_len >= 512;
 #if defined(FB_BLOCK_CFG_BIG) && defined(FB_BLOCK_CFG_SMALL)
   // build-time override (used to sweep configurations)
-  return rows >= 1024 ? FB_BLOCK_CFG_BIG : FB_BLOCK_CFG_SMALL;
+  return key_groups ? FB_BLOCK_CFG_BIG : FB_BLOCK_CFG_SMALL;
 #else
-  // measured on MI355X: blocks of 1024 rows and more per KV head take
-  // workgroups in two key groups: 64 rows (four 32-row waves, two
-  // workgroups per CU, 12-20% faster than eight 16-row waves on small grids)
-  // or, for the 1560-row video frame, 80 rows (ten 16-row waves, one per
-  // CU: 25.3 against 31.1 us for eight 16-row waves, 29.8 for 64 rows).
+  // measured on MI355X: blocks of 1024 rows and more per KV head, and
+  // blocks of 512 keys and more, take workgroups in two key groups: 64 rows
+  // (four 32-row waves, two workgroups per CU) or 80 rows (ten 16-row waves,
+  // one per CU).  80 rows wherever they need fewer workgroups per CU than 64
+  // rows: the 1560-row video frame, 240 workgroups against 300, 25.3 against
+  // 29.8 us; two frames, 480 against 600, 49.3 against 53.6.  With as many
+  // per CU, the two concurrent 64-row workgroups win (32 heads x 768
+  // tokens, 384 against 320: 19.1 against 28.5 us; 8 heads x 1560, 200
+  // against 160: 24.1 against 24.5).  Against the 32-row text workgroups,
+  // key groups gain 9-33% from 512 keys up (32 x 768 tokens: 28.3 -> 19.1
+  // us) and lose below 200 (GQA 32/8 x 160 tokens: 6.9 -> 8.0).
   // Text blocks are latency-bound and run fastest on
   // 4-wave workgroups whose extra waves only issue tile loads: 16 rows (one
   // row wave) while that gives at most one workgroup per CU, else 32 rows
   // (two row waves), which beat 16-row ones once those fill the CUs twice.
-  if (rows >= 1024) {
-    // 80-row workgroups of ten 16-row waves in two key groups, one per CU,
-    // wherever the 64-row ones would leave some CUs with two or more (the
-    // 1560-row video frame: 300 workgroups of 64 rows, 240 of 80; two
-    // frames: 600 and 480, 49.3 against 53.6 us); the busiest SIMD then
-    // holds three 16-row waves over half the keys instead of two 32-row
-    // ones.  Grids of at most one 64-row workgroup per CU keep 64 rows
-    // (8 heads x 1560 rows: 24.1 against 24.5 us).
+  if (key_groups) {
     const int64_t wgs64 = (int64_t)d->batch * d->hkv * ceil_div(rows, 64);
-    return wgs64 > kCUs ? fb::CFG_B80_K2 : fb::CFG_B64_K2;
+    const int64_t wgs80 = (int64_t)d->batch * d->hkv * ceil_div(rows, 80);
+    return ceil_div(wgs80, kCUs) < ceil_div(wgs64, kCUs) ? fb::CFG_B80_K2 : fb::CFG_B64_K2;
   }
   const int64_t wgs16 = (int64_t)d->batch * d->hkv * ceil_div(rows, 16);
   return wgs16 <= kCUs ? fb::CFG_B16_LD : fb::CFG_B32_LD;

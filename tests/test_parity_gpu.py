@@ -147,15 +147,17 @@ def test_text_gqa_sparse(r):
 @pytest.mark.parametrize("batch,hq,hkv,lb,mode", [(2, 2, 2, 1100, "cached"), (2, 8, 2, 300, "cached"),
                                                   (2, 8, 2, 300, "full"), (1, 16, 16, 1190, "cached"),
                                                   (1, 16, 16, 1025, "cached"), (1, 64, 16, 300, "cached"),
-                                                  (2, 8, 8, 1190, "full"), (1, 24, 24, 1100, "cached")])
+                                                  (2, 8, 8, 1190, "full"), (1, 32, 32, 1100, "cached"),
+                                                  (1, 8, 8, 600, "cached")])
 def test_big_block_ragged_streams(batch, hq, hkv, lb, mode):
     """Blocks of >= 1024 query rows per KV head (the key-group block
     configurations), MHA and GQA, over ragged streams, cached and full.  The
-    last five need more than 256 workgroups of 64 rows, so they run the
-    80-row form: ragged in rows and keys (1190), a last key tile of one key,
-    which the second key group sees fully masked (1025), 80-row tiles that
-    straddle query heads (GQA 64/16, 300 tokens), two ragged streams in full
-    mode, and 336 workgroups of 80 rows, more than one round (24 x 1100)."""
+    next five need fewer rounds of 80-row workgroups than of 64-row ones,
+    so they run the 80-row form: ragged in rows and keys (1190), a last key
+    tile of one key, which the second key group sees fully masked (1025),
+    80-row tiles that straddle query heads (GQA 64/16, 300 tokens), two
+    ragged streams in full mode, and 448 workgroups of 80 rows, two rounds
+    (32 x 1100).  The last has 600 rows but 600 keys: 64-row key groups."""
     w = wl.Workload("big", "bf16", batch, hq, hkv, 128, lb, 300, 3, 1.0, 0.1, ragged=0.25, seed=97)
     prefix, blocks = wl.make_inputs(w)
     check_block(w, prefix, blocks[0], 2, mode)
