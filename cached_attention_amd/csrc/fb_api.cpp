@@ -323,6 +323,11 @@ fb_status run_combine(const fb_desc* d, int chunk_mode, const fb_sparse* sp, con
   if (unit_plan) c.total_splits = p.total_splits * d->hkv;
   c.Hkv = d->hkv;
   c.G = d->hq / d->hkv;
+  c.max_splits = 0;
+  for (int b = 0; b < d->batch; ++b)
+    c.max_splits = (int32_t)std::max<int64_t>(c.max_splits, ceil_div(logical_tiles_host(d, b, chunk_mode, n_sel,
+                                                                                        p.chunk_tiles), p.split_tiles));
+  if (unit_plan) c.max_splits = p.total_splits * d->hkv;   // the plan's split lengths are decided on the device
   const int64_t rows = (int64_t)d->batch * d->hq * d->block_len;
   return hip_status(fb::launch_combine(c, rows, stream), "split combine launch");
 }

@@ -111,7 +111,9 @@ struct CombineArgs {
   float* lse;              // [B][Hq][Lb]
   const int32_t* plan;     // unit plan (nullable = every head): rows of unlisted heads are left untouched
   int32_t Hkv, G;
+  int32_t max_splits;      // most splits of any stream (without a unit plan; the plan's are unknown on the host)
 };
+constexpr int kFewSplits = 4;   // rows of at most this many splits take the one-round-trip combine
 
 // Unit plan of a masked step, int32 in device memory, written by
 // launch_unit_plan from a [B][Hkv] recompute mask (P = B * Hkv pairs):

@@ -1333,6 +1333,74 @@ __device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, i
   if (lane == 0) c.lse[row] = any ? mx + logf(wsum) : kNegInf;
 }
 
+// Rows of at most kFewSplits splits, without a unit plan (the video frame's
+// prefix pass: three): one row per group of D/4 lanes (4 dims each), so a
+// wave combines 64 / (D/4) rows, and every load of a row -- the split LSEs,
+// all partial rows and the extra partial -- is issued before the first of
+// them is used: one memory round trip per row instead of two, and half (D =
+// 128) or a quarter (D = 64) of the waves.  Same weights and result as
+// combine_row; the splits are summed in order.
+template <int D>
+__global__ void __launch_bounds__(256) combine_few_kernel(const CombineArgs c, int64_t rows) {
+  constexpr int LPR = D / 4;        // lanes per row
+  constexpr int RPW = 64 / LPR;     // rows per wave
+  static_assert(LPR >= kFewSplits, "a row's split weights live in its own lane group");
+  const int lane = threadIdx.x & 63;
+  const int q = lane / LPR;
+  const int li = lane % LPR;
+  const int d0 = 4 * li;
+  const int64_t hl = (int64_t)c.Hq * c.Lb;
+  for (int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW; base < rows;
+       base += (int64_t)gridDim.x * 4 * RPW) {
+    const int64_t row = base + q;
+    const bool valid = row < rows;   // uniform over the row's lane group
+    const int b = valid ? (int)(row / hl) : 0;
+    const int64_t rem = row % hl;
+    int x0 = 0;
+    for (int bb = 0; bb < b; ++bb) x0 += splits_of(c.offsets, bb, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles);
+    int ns = valid ? splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles) : 0;
+    if (x0 > c.total_splits) x0 = c.total_splits;
+    if (ns > c.total_splits - x0) ns = c.total_splits - x0;
+    if (ns > kFewSplits) ns = kFewSplits;   // the host chose this kernel only when no stream has more
+    // every load of the row first
+    const float ls = li < ns ? c.part_lse[(int64_t)(x0 + li) * hl + rem] : kNegInf;   // lane li: split li's LSE
+    f32x4 v[kFewSplits];
+#pragma unroll
+    for (int x = 0; x < kFewSplits; ++x) {
+      v[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (x < ns) v[x] = *(const f32x4*)(c.part_o + ((int64_t)(x0 + x) * hl + rem) * D + d0);
+    }
+    const bool ext = valid && c.extra_lse != nullptr;
+    const float le = ext ? c.extra_lse[row] : kNegInf;
+    f32x4 ve = {0.f, 0.f, 0.f, 0.f};
+    if (ext) ve = *(const f32x4*)(c.extra_o + row * D + d0);
+    // max over the row's splits and the extra partial (within the lane group)
+    float mx = fmaxf(ls, le);
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    const float wl = (li < ns && mx != kNegInf) ? expf(ls - mx) : 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+#pragma unroll
+    for (int x = 0; x < kFewSplits; ++x) {
+      const float w = __shfl(wl, q * LPR + x, 64);   // 0 past the row's last split
+      wsum += w;
+      acc = w * v[x] + acc;
+    }
+    if (mx != kNegInf && ext) {
+      const float w = expf(le - mx);
+      wsum += w;
+      acc = w * ve + acc;
+    }
+    const bool any = wsum > 0.f;
+    const float inv = any ? 1.f / wsum : 0.f;
+    if (valid) {
+      *(f32x4*)(c.o + row * D + d0) = acc * inv;
+      if (li == 0) c.lse[row] = any ? mx + logf(wsum) : kNegInf;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // two-partial merge: one wave per row (all reads of a row precede its writes)
 // ---------------------------------------------------------------------------
@@ -2165,6 +2233,15 @@ int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partia
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
+  if (!c.plan && c.max_splits <= kFewSplits) {
+    const int64_t rpw = c.D == 64 ? 4 : 2;   // rows per wave
+    const dim3 grid = capped_grid((rows + 4 * rpw - 1) / (4 * rpw));
+    if (c.D == 64)
+      hipLaunchKernelGGL((combine_few_kernel<64>), grid, dim3(256), 0, s, c, rows);
+    else
+      hipLaunchKernelGGL((combine_few_kernel<128>), grid, dim3(256), 0, s, c, rows);
+    return (int)hipGetLastError();
+  }
   const dim3 grid = capped_grid((rows + 3) / 4);
   if (c.D == 64)
     hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, s, c, rows);
