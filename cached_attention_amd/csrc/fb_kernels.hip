@@ -1340,11 +1340,11 @@ __device__ __forceinline__ void combine_row(const CombineArgs& c, int64_t row, i
 // them is used: one memory round trip per row instead of two, and half (D =
 // 128) or a quarter (D = 64) of the waves.  Same weights and result as
 // combine_row; the splits are summed in order.
-template <int D>
+template <int D, int NSPL>
 __global__ void __launch_bounds__(256) combine_few_kernel(const CombineArgs c, int64_t rows) {
   constexpr int LPR = D / 4;        // lanes per row
   constexpr int RPW = 64 / LPR;     // rows per wave
-  static_assert(LPR >= kFewSplits, "a row's split weights live in its own lane group");
+  static_assert(LPR >= NSPL, "a row's split weights live in its own lane group");
   const int lane = threadIdx.x & 63;
   const int q = lane / LPR;
   const int li = lane % LPR;
@@ -1361,12 +1361,12 @@ __global__ void __launch_bounds__(256) combine_few_kernel(const CombineArgs c, i
     int ns = valid ? splits_of(c.offsets, b, c.split_tiles, c.chunk_mode, c.n_sel, c.chunk_tiles) : 0;
     if (x0 > c.total_splits) x0 = c.total_splits;
     if (ns > c.total_splits - x0) ns = c.total_splits - x0;
-    if (ns > kFewSplits) ns = kFewSplits;   // the host chose this kernel only when no stream has more
+    if (ns > NSPL) ns = NSPL;   // the host chose this kernel only when no stream has more
     // every load of the row first
     const float ls = li < ns ? c.part_lse[(int64_t)(x0 + li) * hl + rem] : kNegInf;   // lane li: split li's LSE
-    f32x4 v[kFewSplits];
+    f32x4 v[NSPL];
 #pragma unroll
-    for (int x = 0; x < kFewSplits; ++x) {
+    for (int x = 0; x < NSPL; ++x) {
       v[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
       if (x < ns) v[x] = *(const f32x4*)(c.part_o + ((int64_t)(x0 + x) * hl + rem) * D + d0);
     }
@@ -1382,7 +1382,7 @@ __global__ void __launch_bounds__(256) combine_few_kernel(const CombineArgs c, i
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
 #pragma unroll
-    for (int x = 0; x < kFewSplits; ++x) {
+    for (int x = 0; x < NSPL; ++x) {
       const float w = __shfl(wl, q * LPR + x, 64);   // 0 past the row's last split
       wsum += w;
       acc = w * v[x] + acc;
@@ -2230,16 +2230,33 @@ int launch_attn(const AttnArgs& a, int dtype, int head_dim, int cfg, bool partia
   return head_dim == 64 ? launch_bf16_cfg<64>(a, cfg, s) : launch_bf16_cfg<128>(a, cfg, s);
 }
 
+#ifndef FB_COMBINE_MANY
+#define FB_COMBINE_MANY 1
+#endif
+constexpr int64_t kFewRowsManySplits = 4096;   // rows up to which 17-32 splits go in one round trip
 int launch_combine(const CombineArgs& c, int64_t rows, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  if (!c.plan && c.max_splits <= kFewSplits) {
+  // every load of a row in one round trip (combine_few_kernel): rows of at
+  // most 4 splits, and at head_dim 128 few rows (at most 4096) of 17-32
+  // splits, where one wave per row leaves the CUs nearly empty.  Measured on
+  // MI355X (graph-replayed): video frame, 3 splits, 12.0 -> 7.5 us; 128K
+  // GQA, 32 splits x 2048 rows, 7.95 -> 6.37; the sparse step's 30 selected
+  // splits 6.5 -> 5.3; slower at 16 splits x 1024 rows (32K MHA, 4.2 -> 4.5)
+  // and 8 splits x 8192 rows (the ragged batch, 9.55 -> 9.67), which keep
+  // one wave per row.
+  const bool many = c.D == 128 && rows <= kFewRowsManySplits && c.max_splits > 16 && c.max_splits <= 32;
+  if (!c.plan && (c.max_splits <= kFewSplits || (FB_COMBINE_MANY && many))) {
     const int64_t rpw = c.D == 64 ? 4 : 2;   // rows per wave
     const dim3 grid = capped_grid((rows + 4 * rpw - 1) / (4 * rpw));
-    if (c.D == 64)
-      hipLaunchKernelGGL((combine_few_kernel<64>), grid, dim3(256), 0, s, c, rows);
-    else
-      hipLaunchKernelGGL((combine_few_kernel<128>), grid, dim3(256), 0, s, c, rows);
+    if (c.max_splits <= kFewSplits) {
+      if (c.D == 64)
+        hipLaunchKernelGGL((combine_few_kernel<64, kFewSplits>), grid, dim3(256), 0, s, c, rows);
+      else
+        hipLaunchKernelGGL((combine_few_kernel<128, kFewSplits>), grid, dim3(256), 0, s, c, rows);
+    } else {
+      hipLaunchKernelGGL((combine_few_kernel<128, 32>), grid, dim3(256), 0, s, c, rows);
+    }
     return (int)hipGetLastError();
   }
   const dim3 grid = capped_grid((rows + 3) / 4);

@@ -248,6 +248,7 @@ def _custom(dtype, batch, hq, hkv, d, lb, lens, steps=2, seed=99):
     dict(batch=2, hq=8, hkv=2, d=64, lb=48, lens=[900, 70]),       # 192 rows at D=64: one 256-row prefix tile
     dict(batch=1, hq=2, hkv=2, d=64, lb=1100, lens=[300]),         # 1100 rows at D=64: 64-row key-group block pass
     dict(batch=1, hq=16, hkv=16, d=64, lb=1190, lens=[200]),       # 16 x 1190 rows at D=64: 80-row key-group block pass
+    dict(batch=1, hq=32, hkv=8, d=128, lb=8, lens=[6400]),         # 25 splits of 4 tiles: the 32-split combine
     dict(batch=2, hq=2, hkv=2, d=128, lb=1100, lens=[0, 90]),      # 64-row key groups, one stream without prefix
     dict(batch=2, hq=16, hkv=16, d=128, lb=1190, lens=[150, 0]),   # 80-row key groups, one stream without prefix
 ])
