@@ -2115,6 +2115,16 @@ __global__ void __launch_bounds__(kPlanThreads) unit_plan_kernel(const UnitPlanA
     tot += t;
     mx = t > mx ? t : mx;
   }
+  if (n == 0) {   // nothing recomputed (uniform): an empty plan, no split search
+    if (tid == 0) {
+      base[0] = 0;
+      u.plan[0] = 0;
+      u.plan[1] = u.min_split;
+      u.plan[2] = 0;
+      u.plan[3] = 0;
+    }
+    return;
+  }
   wg_sum_max64(tot, mx, red);
   // split length: total tiles of the listed pairs over the cap, raised until
   // their splits' workgroups fit (or one split per pair)
