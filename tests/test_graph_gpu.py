@@ -16,10 +16,15 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device="cuda", dtype=torch.bfloat16)
 
 
-@pytest.mark.parametrize("sparse", [False, True])
-def test_block_graph_replays_match_eager(sparse):
-    w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=1500, hq=8, hkv=2, block_len=16, batch=2)
-    w = wl.replace(w, ragged=0.25, steps=4)
+@pytest.mark.parametrize("shape,sparse", [("text", False), ("text", True), ("frame", False)],
+                         ids=["text", "text_sparse", "frame"])
+def test_block_graph_replays_match_eager(shape, sparse):
+    if shape == "text":
+        w = wl.ci_version(wl.WORKLOADS["text_gqa_128k"], prefix_len=1500, hq=8, hkv=2, block_len=16, batch=2)
+        w = wl.replace(w, ragged=0.25, steps=4)
+    else:   # 16 heads x 1190-token block: the 80-row key-group block pass
+        w = wl.ci_version(wl.WORKLOADS["video_1560"], prefix_len=600, hq=16, hkv=16, block_len=1190, n_blocks=1)
+        w = wl.replace(w, steps=4)
     prefix, blocks = wl.make_inputs(w)
     blk = blocks[0]
     chunks = torch.tensor([[[0, 7], [3, 11]], [[2, 5], [1, 9]]], dtype=torch.int32) if sparse else None
