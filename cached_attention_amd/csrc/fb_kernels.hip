@@ -99,7 +99,7 @@ __device__ __forceinline__ int splits_of(const int64_t* off, int b, int split_ti
 // ---------------------------------------------------------------------------
 
 struct TileIter {
-  int lt, lt_end;
+  int lt, lt_end, step;   // logical tiles lt, lt + step, ... below lt_end (step > 1: interleaved splits)
   int64_t lp;
   const int32_t* list;
   int nlist, ptr, mode, ct;
@@ -111,7 +111,8 @@ template <bool DENSE = false>
 __device__ __forceinline__ bool next_tile(TileIter& it, int64_t& tok0, int& nvalid) {
   if (DENSE || it.mode == CHUNKS_ALL) {   // wave-uniform: one scalar branch per tile
     if (it.lt >= it.lt_end) return false;
-    const int64_t start = (int64_t)(it.lt++) * kTile;
+    const int64_t start = (int64_t)it.lt * kTile;
+    it.lt += it.step;
     tok0 = start;
     const int64_t rem = it.lp - start;
     nvalid = rem < kTile ? (int)rem : kTile;
@@ -153,12 +154,13 @@ struct Work {
   const char* vbase;
 };
 
-template <int ESZ>
+template <int ESZ, bool INTERLEAVE = false>
 __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
   const int L = blockIdx.x;
   const int per = a.grid >> 3;
   const int w = (L & 7) * per + (L >> 3);
   TileIter& it = wk.it;
+  it.step = 1;
   it.list = nullptr;
   it.nlist = 0;
   it.ptr = 0;
@@ -204,11 +206,12 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
   wk.x = gx / a.Hkv;
   wk.h_off = wk.g * a.G;
   if (a.offsets) {
-    int acc = 0, b = 0, j = 0;
+    int acc = 0, b = 0, j = 0, nsb = 0;
     for (; b < a.B; ++b) {
       const int ns = splits_of(a.offsets, b, a.split_tiles, a.chunk_mode, a.n_sel, a.chunk_tiles);
       if (wk.x < acc + ns) {
         j = wk.x - acc;
+        nsb = ns;
         break;
       }
       acc += ns;
@@ -217,8 +220,17 @@ __device__ __forceinline__ bool decode_work(const AttnArgs& a, Work& wk) {
     wk.b = b;
     it.lp = prefix_len(a.offsets, b);
     const int nl = logical_tiles(a.offsets, b, a.chunk_mode, a.n_sel, a.chunk_tiles);
-    it.lt = j * a.split_tiles;
-    it.lt_end = min(nl, it.lt + a.split_tiles);
+    if (INTERLEAVE && a.chunk_mode == CHUNKS_ALL) {
+      // split j of the stream's nsb takes tiles j, j + nsb, j + 2 nsb, ...:
+      // at most split_tiles of them, and the splits of a KV head read
+      // neighbouring tiles at the same time
+      it.lt = j;
+      it.lt_end = nl;
+      it.step = nsb;
+    } else {
+      it.lt = j * a.split_tiles;
+      it.lt_end = min(nl, it.lt + a.split_tiles);
+    }
     it.mode = a.chunk_mode;
     if (a.chunk_mode != CHUNKS_ALL) {
       it.list = a.chunks + ((int64_t)b * a.Hkv + wk.g) * a.n_sel;
@@ -397,6 +409,9 @@ __device__ __forceinline__ void mfma_prio() {
   if constexpr (FB_MFMA_PRIO != 0) __builtin_amdgcn_s_setprio(P);
 }
 
+#ifndef FB_INTERLEAVE_P256
+#define FB_INTERLEAVE_P256 1
+#endif
 template <int D, int QT, int NW, int NS, int MINW, bool PARTIAL, int RW, int KG>
 __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   constexpr int KS = D / 32;                  // k-steps of the score MFMA
@@ -427,8 +442,10 @@ __global__ void __launch_bounds__(64 * NW, MINW) attn_bf16(const AttnArgs a) {
   static_assert((DIST - 1) * IPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
+  // interleaved splits for the 256-row split-KV pass (see decode_work)
+  constexpr bool kInterleave = FB_INTERLEAVE_P256 != 0 && PARTIAL && QT == 2 && NW == 8 && KG == 1;
   Work wk;
-  if (!decode_work<2>(a, wk)) return;
+  if (!decode_work<2, kInterleave>(a, wk)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
