@@ -269,11 +269,13 @@ def test_edge_shapes(dtype, case):
 def test_score_jump_reruns_pass(dtype, shape):
     """Scores far above a pass's first-tile maxima (the kernel's softmax reference).
 
-    Prefix: 6 tiles, split as tiles 0-3 and 4-5 (splits of at least 4 tiles);
-    a large key in tile 3 and one in tile 5 give some rows scores more than
-    64 log2 units above their split's first-tile maxima, which sends the bf16
-    pass through its rerun against the split's exact maxima, from each
-    split-KV layout's own main loop.  Block (when it has a second tile): the
+    Prefix: 6 tiles in two splits (splits of at least 4 tiles): tiles 0-3
+    and 4-5, or, in the 256-row layout, which interleaves its splits, tiles
+    0, 2, 4 and 1, 3, 5; a large key in tile 3 and one in tile 5 give some
+    rows scores more than 64 log2 units above their split's first-tile
+    maxima (any ordinary tile's maxima are far below the spike), which sends
+    the bf16 pass through its rerun against the split's exact maxima, from
+    each split-KV layout's own main loop.  Block (when it has a second tile): the
     same in its second tile (key 80), and for blocks of 1024 rows and more,
     whose waves split every tile into two 32-key halves, also in the second
     half of its third tile (key 168).  Results must still match the oracle.
