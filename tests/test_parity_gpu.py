@@ -290,7 +290,7 @@ def test_score_jump_reruns_pass(dtype, shape):
     # precondition: some row's spike score clears its first tile's max by > 64 (log2)
     scale, log2e = scale_of(w), 1.0 / math.log(2.0)
     q = blk.q.astype(np.float64).reshape(-1, w.head_dim)
-    for spike_tok, first_tile in ((200, 0), (330, 4)):
+    for spike_tok, first_tile in ((200, 0), (330, 4), (200, 1), (330, 1)):   # first tiles of both layouts' splits
         first = (q @ prefix.k[64 * first_tile:64 * first_tile + 64, 0].astype(np.float64).T).max(axis=1)
         spike = q @ prefix.k[spike_tok, 0].astype(np.float64)
         assert ((spike - first) * scale * log2e > 64).any()
